@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the decompression hot path on one MI355X.
+
+A step is one df_decompress of a whole Llama-3-8B-shaped transformer block
+(q, k, v, o, gate, up, down: 218,103,808 BF16 weights, one codebook, one
+launch) from device-resident compressed sections into a BF16 buffer.  The
+compressed inputs are rotated over several device copies and the output over
+two buffers, so each step reads inputs that the 256 MB Infinity Cache does
+not hold.  Prints one JSON line:
+
+  value      decompressed BF16 GB/s = 2 n K / wall time of K steps
+  roofline   algorithmic HBM bytes of one launch (stream bytes + sign|mantissa
+             bytes + gap bits + tile offsets read, 2 n written) / the
+             launch's mean duration from HIP events on its stream, against
+             8 TB/s
+  cpu_baseline  the CPU oracle's decode of the same container on the host
+             cores (tile ranges on threads), a plain bit-serial reference
+
+Other workloads (--workload) are for local measurement; the default is the
+8B BF16 block.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+METRIC = "decompressed BF16 GB/s (+% of HBM roofline), 8B-shaped transformer block"
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(inf) -> int:
+    """Bytes one launch must move: the used stream, the gap fields, the tile
+    offsets and (BF16) the sign|mantissa plane read; the output written."""
+    n = int(inf["n"])
+    read = (int(inf["total_bits"]) + 7) // 8 + (5 * int(inf["n_threads"]) + 7) // 8 \
+        + 8 * (int(inf["n_tiles"]) + 1)
+    if int(inf["kind"]) == 0:
+        read += n
+        write = 2 * n
+    else:
+        write = n
+    return read + write
+
+
+def make_workload(name: str, seed: int):
+    from lossless_entropy_coded_huffman_amd import synth
+    if name == "llama3_8b_block_bf16":
+        src, _ = synth.bf16_block(seed)
+        return 0, [src], {"matrices": "q,k,v,o,gate,up,down", "shapes": "Llama-3-8B block",
+                          "dist": "N(0,s^2), s~U[0.01,0.04] per matrix"}
+    if name == "c1_1m_bf16":
+        return 0, [synth.c1_tensor(seed)], {"dist": "N(0,0.02^2)"}
+    if name == "llama3_8b_block_u8":
+        layers = synth.u8_block(seed)
+        return 1, [q for _, q, _ in layers], {"matrices": "q,k,v,o,gate,up,down",
+                                              "quantizers": "".join("A" if a else "U" for _, _, a in layers)}
+    if name == "llama31_405b_block_t3_bf16":
+        src, _ = synth.bf16_block(seed, config=synth.CONFIG_405B, shapes=synth.LLAMA31_405B_BLOCK,
+                                  dist="t3")
+        return 0, [src], {"matrices": "q,k,v,o,gate,up,down", "shapes": "Llama-3.1-405B block",
+                          "dist": "Student-t(3)*0.02/sqrt(3)"}
+    raise SystemExit("unknown workload " + name)
+
+
+def cpu_baseline(containers, srcs, kind):
+    import oracle
+    cores = max(1, min(16, os.cpu_count() or 1))
+    total = sum(int(c.info()["n"]) for c in containers)
+    out_bytes = total * (2 if kind == 0 else 1)
+    dicts = []
+    for c in containers:
+        inf = c.info()
+        d = {k: np.asarray(c.section(k)) for k in ("bitstream", "gaps", "tile_out", "sign_mantissa")}
+        d.update(kind=inf["kind"], n=inf["n"], n_tiles=inf["n_tiles"], n_threads=inf["n_threads"],
+                 lengths=inf["lengths"])
+        dicts.append(d)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        outs = [oracle.decode_tiles(d, cores) for d in dicts]
+        times.append(time.perf_counter() - t0)
+    ok = all(np.array_equal(o, s) for o, s in zip(outs, srcs))
+    t_mt = statistics.median(times)
+    # one thread on the first sixteenth of the tiles of the first container
+    d0 = dict(dicts[0])
+    nt = max(1, int(d0["n_tiles"]) // 16)
+    d0["n_tiles"] = nt
+    d0["n"] = int(d0["tile_out"][nt])
+    d0["tile_out"] = d0["tile_out"][: nt + 1]
+    t0 = time.perf_counter()
+    o1 = oracle.decode_tiles(d0, 1)
+    t_1 = time.perf_counter() - t0
+    ok = ok and np.array_equal(o1, srcs[0][: d0["n"]])
+    esz = 2 if kind == 0 else 1
+    return {
+        "value": round(out_bytes / t_mt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": "the whole workload's containers, oracle bit-serial decode over contiguous tile "
+                  "ranges on %d threads, median of 3 runs; single-thread figure on the first 1/16 "
+                  "of the tiles (%d elements)" % (cores, d0["n"]),
+        "value_1thread": round(d0["n"] * esz / t_1 / 1e9, 4), "verified": bool(ok),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=3, help="device copies of the compressed input")
+    ap.add_argument("--workload", default="llama3_8b_block_bf16",
+                    choices=["llama3_8b_block_bf16", "c1_1m_bf16", "llama3_8b_block_u8",
+                             "llama31_405b_block_t3_bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the codec needs no collectives and this build "
+              "measures the single-GPU decode (a multi-GPU run would shard whole transformer "
+              "blocks across GPUs with no exchange step).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lossless_entropy_coded_huffman_amd as dfh
+    from lossless_entropy_coded_huffman_amd import build_lib
+
+    if not os.path.exists(build_lib.LIB):
+        build_lib.build()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU")
+    dev = torch.device("cuda:0")
+
+    log("workload", args.workload, "seed", args.seed)
+    kind, srcs, wconf = make_workload(args.workload, args.seed)
+    n = sum(s.size for s in srcs)
+    t0 = time.perf_counter()
+    containers = [dfh.compress(kind, s) for s in srcs]
+    log("compressed in %.2f s" % (time.perf_counter() - t0))
+    infos = [c.info() for c in containers]
+    copies = [[dfh.to_device(c, dev) for c in containers] for _ in range(max(1, args.copies))]
+    outs = [[dc.empty_output() for dc in copies[0]] for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k):
+        dcs = copies[k % len(copies)]
+        o = outs[k % 2]
+        if len(dcs) == 1:
+            dfh.df_decompress(dcs[0], o[0], stream)
+        else:
+            dfh.df_decompress_batch(dcs, o, stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step(k)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    # bit-exact check of both output buffers after the timed region
+    verified = True
+    for o in outs:
+        for s, t in zip(srcs, o):
+            ref = torch.from_numpy(s.view(np.int16) if kind == 0 else s).to(dev)
+            got = t.view(torch.int16) if kind == 0 else t
+            verified = verified and bool(torch.equal(got, ref))
+
+    out_bytes = n * (2 if kind == 0 else 1)
+    value = out_bytes * args.steps / wall / 1e9
+    mean_ms = statistics.mean(launch_ms)
+    alg = sum(algorithmic_bytes(i) for i in infos)
+    achieved = alg / (mean_ms * 1e-3) / 1e9
+    stored = sum(dc.compressed_bytes() for dc in copies[0])
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        try:
+            prof = json.load(open(PROFILE_COUNTERS))
+            entry = prof.get(args.workload)
+            if entry and entry.get("kernel_source_sha") == kernel_sha():
+                traffic = entry["bytes_per_launch"]
+        except (ValueError, KeyError):
+            traffic = None
+    line = {
+        "metric": METRIC if args.workload == "llama3_8b_block_bf16" else
+        METRIC.replace("8B-shaped transformer block", args.workload),
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic",
+        "config": dict({"workload": args.workload, "elements": int(n), "containers": len(containers),
+                        "output": "bf16" if kind == 0 else "uint8", "seed": args.seed,
+                        "stored_bytes": int(stored), "stored_over_raw": round(stored / out_bytes, 4),
+                        "input_copies": len(copies)}, **wconf),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(alg), "launch_ms_mean": round(mean_ms, 5),
+                     "launch_ms_min": round(min(launch_ms), 5)},
+        "verified": verified,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(containers, srcs, kind)
+    print(json.dumps(line), flush=True)
+    if not verified:
+        sys.exit(1)
+
+
+def kernel_sha() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "lossless_entropy_coded_huffman_amd", "csrc", "dfh_decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * dfh.h -- C ABI of the lossless Huffman weight codec for AMD MI355X (gfx950).
+ *
+ * What the library does.  The DFloat11 digest ("DFloat11: compressao sem
+ * perda para inferencia em GPU que reduz LLMs para 70% do tamanho",
+ * pt.news.hada.io) and its paper's abstract ("70% Size, 100% Accuracy:
+ * Lossless LLM Compression for Efficient GPU Inference via Dynamic-Length
+ * Float") describe BF16 weights whose 8-bit exponent is Huffman coded while
+ * sign and mantissa are stored raw, decompressed losslessly on the GPU just
+ * before each transformer block runs.  The EntroLLM summary ("EntroLLM:
+ * Entropy Encoded Weight Compression for Efficient Large Language Model
+ * Inference on Edge Devices", section "Metodologia") Huffman codes whole
+ * uint8 quantised weights and decodes them in parallel.  This library covers
+ * both: DF_KIND_BF16 codes the exponent byte, DF_KIND_U8 codes the byte.
+ *
+ * Host calls build a codebook and encode into a library-owned container;
+ * device calls decompress a container whose sections the caller has copied
+ * to device memory.
+ *
+ * Conventions for every call:
+ *   - Returns df_status; nothing throws across the ABI.
+ *   - Pointers are borrowed for the duration of the call unless stated.
+ *   - Host calls are reentrant; containers are immutable after df_encode or
+ *     df_container_load and may be read from several threads.
+ *   - Device calls enqueue work on the given HIP stream and return without
+ *     synchronising, allocating, or copying between host and device.
+ *
+ * Container format (little-endian).  Element i has symbol e_i (the BF16
+ * exponent byte (u >> 7) & 0xFF, or the uint8 value).  Codes are canonical
+ * (RFC 1951 section 3.2.2) from lengths[256] (0 = unused, 1..32).  Sections:
+ *   BITSTREAM      codes of e_0, e_1, ... concatenated, packed least
+ *                  significant bit first inside each byte, each code emitted
+ *                  from its most significant bit; n_tiles*2048 + 16 bytes,
+ *                  zero padded.  (Digest, "O formato DFloat11":
+ *                  EncodedExponent.)
+ *   GAPS           5-bit field per decoding thread t (8 stream bytes each),
+ *                  at stream bits [5t, 5t+5), least significant bit first:
+ *                  the offset of the first code that starts at or after bit
+ *                  64t, always 0..31; 0 for t >= n_threads.
+ *                  n_tiles*160 + 16 bytes.  (Digest, "Kernel de GPU em 2
+ *                  etapas e metadados auxiliares": Gaps array.)
+ *   TILE_OUT       uint64[n_tiles + 1]: number of codes starting before bit
+ *                  16384*b (the output index of the first element of thread
+ *                  block b); the last entry is n.  (Same section: one output
+ *                  position per thread block.)
+ *   SIGN_MANTISSA  BF16 only: byte i = (sign << 7) | mantissa7 of element i;
+ *                  round_up(n, 64) bytes, zero padded; 0 bytes for uint8.
+ *                  (Digest, "O formato DFloat11": PackedSignMantissa.)
+ *   LUT            uint16[n_luts * 256]: the code tree cut into height-8
+ *                  subtrees, one 256-entry table each, indexed by the next 8
+ *                  stream bits (first bit = index bit 0).  Entry: leaf =
+ *                  (code length << 8) | symbol; pointer = 0x8000 | table;
+ *                  0xFFFF = no code.  Tables numbered breadth first.
+ *                  (Digest, "Decodificacao com LUT hierarquica".)
+ *   DTAB           uint64[4096], derived from lengths, not stored in files:
+ *                  a decoder-side table indexed by the next 12 stream bits
+ *                  that gives up to five whole codes at once.  Layout:
+ *                  bits 0..39 symbol bytes (BF16: exponent rotated right by
+ *                  one bit), 40..51 start mask, 56..59 bits consumed, 60..63
+ *                  number of codes (0 = first code longer than 12 bits).
+ * n_threads = floor(start of last code / 64) + 1 (0 when n == 0) and
+ * n_tiles = ceil(n_threads / 256).
+ */
+#ifndef DFH_H
+#define DFH_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DF_OK = 0,
+  DF_ERR_ARG = -1,      /* bad argument: null pointer, bad kind, misaligned dst, ... */
+  DF_ERR_ALLOC = -2,    /* host allocation failed */
+  DF_ERR_CODEBOOK = -3, /* no code fits max_len, or an input symbol has no code */
+  DF_ERR_FORMAT = -4,   /* container header or sections inconsistent */
+  DF_ERR_HIP = -5,      /* a HIP runtime call or kernel launch failed */
+  DF_ERR_CORRUPT = -6,  /* container contents fail validation */
+  DF_ERR_IO = -7        /* file could not be read or written */
+} df_status;
+
+typedef enum { DF_KIND_BF16 = 0, DF_KIND_U8 = 1 } df_kind;
+
+typedef enum {
+  DF_SEC_BITSTREAM = 0,
+  DF_SEC_GAPS = 1,
+  DF_SEC_TILE_OUT = 2,
+  DF_SEC_SIGN_MANTISSA = 3,
+  DF_SEC_LUT = 4,
+  DF_SEC_DTAB = 5,
+  DF_SEC_COUNT = 6
+} df_section;
+
+#define DF_MAX_LEN 32           /* longest code; a gap then fits 5 bits        */
+#define DF_BYTES_PER_THREAD 8   /* stream bytes per decoding thread           */
+#define DF_THREADS_PER_TILE 256 /* decoding threads per tile (thread block)   */
+#define DF_TILE_BITS 16384      /* stream bits per tile                       */
+#define DF_MAX_LUTS 64          /* cap on hierarchical tables (32 KiB)        */
+#define DF_DTAB_BITS 12         /* index width of the multi-code table        */
+#define DF_MAX_BATCH 16         /* containers per df_decompress_batch launch  */
+
+/* Device error bits written by df_decompress_checked. */
+#define DF_DEVERR_COUNT 1u  /* a tile decodes to a different count than tile_out says */
+#define DF_DEVERR_CODE 2u   /* a stream prefix matches no code                      */
+
+typedef struct {
+  df_kind kind;
+  uint32_t max_len;
+  uint64_t n;              /* elements                                  */
+  uint64_t total_bits;     /* sum of code lengths                       */
+  uint64_t n_threads;      /* decoding threads that own a code start    */
+  uint64_t n_tiles;        /* ceil(n_threads / 256)                     */
+  uint32_t n_luts;         /* hierarchical tables                       */
+  uint32_t max_tile_elems; /* largest tile_out[b+1] - tile_out[b]       */
+  uint32_t bytes_per_thread;
+  uint32_t threads_per_tile;
+  uint64_t section_bytes[DF_SEC_COUNT];
+  uint8_t lengths[256];
+} df_info;
+
+typedef struct df_container df_container; /* opaque, library-owned */
+
+/* Histogram of the coded symbol (digest, "O formato DFloat11": the tree
+ * follows the distribution of exponent values).  src holds n uint16 BF16
+ * bit patterns (DF_KIND_BF16) or n bytes (DF_KIND_U8); hist receives 256
+ * counts.  Multi-threaded on the host.  DF_ERR_ARG on a null pointer (src
+ * may be null when n == 0) or a bad kind. */
+df_status df_histogram(df_kind kind, const void *src, uint64_t n, uint64_t hist[256]);
+
+/* Code lengths from a histogram (digest, "O formato DFloat11": frequent
+ * exponents get short codes; "Kernel de GPU em 2 etapas e metadados
+ * auxiliares": codes are at most 32 bits).  Huffman's construction merging
+ * the two smallest (weight, key) nodes, leaves keyed by symbol and merged
+ * nodes by 256 + creation order; when its longest code exceeds max_len, the
+ * optimal max_len-limited lengths by package-merge.  One used symbol gets
+ * length 1; none gives all zeros.  lengths[s] = 0 for unused symbols.
+ * DF_ERR_ARG for max_len outside 1..32; DF_ERR_CODEBOOK when 2^max_len is
+ * below the number of used symbols. */
+df_status df_build_codebook(const uint64_t hist[256], uint32_t max_len, uint8_t lengths[256]);
+
+/* Encode n elements with the given lengths into a new container (*out,
+ * freed with df_container_free).  Builds every section described above.
+ * DF_ERR_CODEBOOK when an element's symbol has length 0 or lengths violate
+ * Kraft's inequality or exceed 32; DF_ERR_ALLOC on allocation failure. */
+df_status df_encode(df_kind kind, const void *src, uint64_t n, const uint8_t lengths[256],
+                    df_container **out);
+
+/* Header scalars, section sizes and lengths of a container. */
+df_status df_container_info(const df_container *c, df_info *out);
+
+/* Pointer to a section's bytes inside the container (valid until
+ * df_container_free) and its size in *nbytes; NULL for a bad argument. */
+const void *df_container_section(const df_container *c, df_section s, uint64_t *nbytes);
+
+/* Write / read a container file (header, then every section except DTAB,
+ * each 64-byte aligned; DTAB is rebuilt on load).  Load validates the
+ * result and returns DF_ERR_FORMAT or DF_ERR_CORRUPT on a bad file. */
+df_status df_container_save(const df_container *c, const char *path);
+df_status df_container_load(const char *path, df_container **out);
+
+/* Structural check of a container: header scalars against each other,
+ * section sizes, lengths (Kraft), tile_out monotone from 0 to n with
+ * max_tile_elems its largest step, gaps in range and zero past n_threads,
+ * LUT and DTAB equal to the tables rebuilt from lengths.  It does not
+ * decode the stream.  DF_ERR_FORMAT or DF_ERR_CORRUPT on failure. */
+df_status df_container_validate(const df_container *c);
+
+void df_container_free(df_container *c);
+const char *df_status_string(df_status s);
+
+/* ------------------------------------------------------------------ device */
+
+/* Borrowed device pointers to a container's sections (caller-owned, e.g.
+ * torch tensors) plus its header scalars.  sign_mantissa is NULL for
+ * DF_KIND_U8.  Every section must have the size df_info reports. */
+typedef struct {
+  df_kind kind;
+  uint32_t n_luts;
+  uint32_t max_tile_elems;
+  uint32_t reserved;
+  uint64_t n;
+  uint64_t total_bits;
+  uint64_t n_threads;
+  uint64_t n_tiles;
+  const uint8_t *bitstream;
+  const uint8_t *gaps;
+  const uint64_t *tile_out;
+  const uint8_t *sign_mantissa;
+  const uint16_t *lut;
+  const uint64_t *dtab;
+} df_device_view;
+
+/* Decompress one container into dst (n * 2 bytes of BF16 bit patterns, or
+ * n bytes of uint8; 16-byte aligned, not aliasing any section).  The
+ * digest's "Kernel de GPU em 2 etapas e metadados auxiliares": each thread
+ * owns 8 stream bytes and decodes the codes that start in them, first only
+ * counting, then (after a prefix sum of the counts over the thread block)
+ * decoding again into an on-chip buffer that is written to memory in one
+ * coalesced pass; "Decodificacao com LUT hierarquica": code tables sit in
+ * on-chip memory.  One launch covers the whole container (the digest's
+ * "Descompressao por bloco de transformer": one batch per block).
+ * n == 0 enqueues nothing.  DF_ERR_ARG on bad pointers, kind, alignment,
+ * or sizes; DF_ERR_HIP when the launch fails. */
+df_status df_decompress(const df_device_view *v, void *dst, hipStream_t stream);
+
+/* As df_decompress, and also checks every tile on the device: d_err (one
+ * device uint32, zeroed by the caller beforehand) receives the OR of
+ * DF_DEVERR_* bits; read it after synchronising the stream.  Output of a
+ * tile that fails a check is unspecified; writes stay inside dst. */
+df_status df_decompress_checked(const df_device_view *v, void *dst, uint32_t *d_err,
+                                hipStream_t stream);
+
+/* Decompress count containers of one kind in a single launch (the EntroLLM
+ * summary, "Metodologia": separate tensors decoded at the same time).  views
+ * is an array of count views, dsts an array of count destinations.  count
+ * may exceed DF_MAX_BATCH; the library then issues several launches.  Same
+ * errors as df_decompress; containers of different kinds give DF_ERR_ARG. */
+df_status df_decompress_batch(const df_device_view *views, void *const *dsts, uint32_t count,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFH_H */

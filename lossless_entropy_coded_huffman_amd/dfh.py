@@ -1,0 +1,327 @@
+"""ctypes binding of libdfh (include/dfh.h), with the same names.
+
+Argument marshalling only: every step of encoding runs in the C++ host
+library and every step of decompression in the HIP kernels.  PyTorch
+provides device memory and streams.  The library is loaded after torch so
+that it binds to the HIP runtime torch has loaded (same soname), and the
+binding refuses to run without the built library: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch  # noqa: F401  (loads the HIP runtime libdfh binds to)
+
+KIND_BF16 = 0
+KIND_U8 = 1
+SEC_BITSTREAM, SEC_GAPS, SEC_TILE_OUT, SEC_SIGN_MANTISSA, SEC_LUT, SEC_DTAB = range(6)
+SECTION_NAMES = ("bitstream", "gaps", "tile_out", "sign_mantissa", "lut", "dtab")
+MAX_LEN = 32
+DEVERR_COUNT = 1
+DEVERR_CODE = 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libdfh.so")
+
+
+class DFError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (what or "dfh", df_status_string(status), status))
+
+
+class df_info(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("max_len", ctypes.c_uint32),
+                ("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64),
+                ("n_threads", ctypes.c_uint64), ("n_tiles", ctypes.c_uint64),
+                ("n_luts", ctypes.c_uint32), ("max_tile_elems", ctypes.c_uint32),
+                ("bytes_per_thread", ctypes.c_uint32), ("threads_per_tile", ctypes.c_uint32),
+                ("section_bytes", ctypes.c_uint64 * 6), ("lengths", ctypes.c_uint8 * 256)]
+
+
+class df_device_view(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("n_luts", ctypes.c_uint32),
+                ("max_tile_elems", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64),
+                ("n_threads", ctypes.c_uint64), ("n_tiles", ctypes.c_uint64),
+                ("bitstream", ctypes.c_void_p), ("gaps", ctypes.c_void_p),
+                ("tile_out", ctypes.c_void_p), ("sign_mantissa", ctypes.c_void_p),
+                ("lut", ctypes.c_void_p), ("dtab", ctypes.c_void_p)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+# name -> (restype, argtypes); the exported C ABI
+_SIGNATURES = {
+    "df_histogram": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+    "df_build_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "df_encode": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_void_p)]),
+    "df_container_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(df_info)]),
+    "df_container_section": (ctypes.c_void_p, [ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_uint64)]),
+    "df_container_save": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p]),
+    "df_container_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]),
+    "df_container_validate": (ctypes.c_int, [ctypes.c_void_p]),
+    "df_container_free": (None, [ctypes.c_void_p]),
+    "df_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "df_decompress": (ctypes.c_int, [ctypes.POINTER(df_device_view), ctypes.c_void_p, ctypes.c_void_p]),
+    "df_decompress_checked": (ctypes.c_int, [ctypes.POINTER(df_device_view), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]),
+    "df_decompress_batch": (ctypes.c_int, [ctypes.POINTER(df_device_view),
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                           ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded libdfh.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libdfh.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+        return _lib
+
+
+def df_status_string(status: int) -> str:
+    return lib().df_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise DFError(status, what)
+
+
+def _host_array(kind: int, src) -> np.ndarray:
+    if isinstance(src, torch.Tensor):
+        src = src.detach().cpu()
+        src = src.view(torch.int16).numpy() if src.dtype == torch.bfloat16 else src.numpy()
+    a = np.ascontiguousarray(src).reshape(-1)
+    want = np.uint16 if kind == KIND_BF16 else np.uint8
+    if a.dtype != want:
+        if a.dtype.itemsize != np.dtype(want).itemsize:
+            raise TypeError("kind %d needs %s elements, got %s" % (kind, np.dtype(want), a.dtype))
+        a = a.view(want)
+    return a
+
+
+# ------------------------------------------------------------------- host API
+def df_histogram(kind: int, src) -> np.ndarray:
+    a = _host_array(kind, src)
+    h = np.zeros(256, np.uint64)
+    _check(lib().df_histogram(kind, a.ctypes.data, a.size, h.ctypes.data), "df_histogram")
+    return h
+
+
+def df_build_codebook(hist, max_len: int = MAX_LEN) -> np.ndarray:
+    h = np.ascontiguousarray(hist, np.uint64)
+    out = np.zeros(256, np.uint8)
+    _check(lib().df_build_codebook(h.ctypes.data, int(max_len), out.ctypes.data), "df_build_codebook")
+    return out
+
+
+class Container:
+    """A library-owned container (df_container*)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("container was freed")
+        return self._h
+
+    def info(self) -> dict:
+        return df_container_info(self)
+
+    def section(self, sec) -> np.ndarray:
+        return df_container_section(self, sec)
+
+    def validate(self):
+        df_container_validate(self)
+
+    def save(self, path: str):
+        df_container_save(self, path)
+
+    def free(self):
+        if self._h:
+            lib().df_container_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def df_encode(kind: int, src, lengths) -> Container:
+    a = _host_array(kind, src)
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    out = ctypes.c_void_p()
+    _check(lib().df_encode(kind, a.ctypes.data if a.size else None, a.size, ln.ctypes.data,
+                           ctypes.byref(out)), "df_encode")
+    return Container(out.value)
+
+
+def df_container_info(c: Container) -> dict:
+    inf = df_info()
+    _check(lib().df_container_info(c.handle, ctypes.byref(inf)), "df_container_info")
+    d = {k: getattr(inf, k) for k, _ in df_info._fields_ if k not in ("section_bytes", "lengths")}
+    d["section_bytes"] = {SECTION_NAMES[i]: int(inf.section_bytes[i]) for i in range(6)}
+    d["lengths"] = np.frombuffer(bytes(inf.lengths), np.uint8).copy()
+    return d
+
+
+_SEC_DTYPE = {SEC_TILE_OUT: np.uint64, SEC_LUT: np.uint16, SEC_DTAB: np.uint64}
+
+
+def df_container_section(c: Container, sec) -> np.ndarray:
+    """Read-only numpy view of a section, valid while the container lives."""
+    if isinstance(sec, str):
+        sec = SECTION_NAMES.index(sec)
+    nbytes = ctypes.c_uint64(0)
+    ptr = lib().df_container_section(c.handle, int(sec), ctypes.byref(nbytes))
+    if ptr is None:
+        raise DFError(-1, "df_container_section")
+    raw = (ctypes.c_uint8 * max(int(nbytes.value), 1)).from_address(ptr)
+    arr = np.frombuffer(raw, np.uint8, count=int(nbytes.value))
+    arr = arr.view(_SEC_DTYPE.get(int(sec), np.uint8))
+    arr.flags.writeable = False
+    # keep the container alive as long as the view
+    return _Owned(arr, c)
+
+
+class _Owned(np.ndarray):
+    def __new__(cls, arr, owner):
+        obj = arr.view(cls)
+        obj._owner = owner
+        return obj
+
+    def __array_finalize__(self, obj):
+        self._owner = getattr(obj, "_owner", None)
+
+
+def df_container_save(c: Container, path: str):
+    _check(lib().df_container_save(c.handle, os.fsencode(path)), "df_container_save")
+
+
+def df_container_load(path: str) -> Container:
+    out = ctypes.c_void_p()
+    _check(lib().df_container_load(os.fsencode(path), ctypes.byref(out)), "df_container_load")
+    return Container(out.value)
+
+
+def df_container_validate(c: Container):
+    _check(lib().df_container_validate(c.handle), "df_container_validate")
+
+
+def df_container_free(c: Container):
+    c.free()
+
+
+def compress(kind: int, src, max_len: int = MAX_LEN) -> Container:
+    """df_histogram -> df_build_codebook -> df_encode."""
+    a = _host_array(kind, src)
+    return df_encode(kind, a, df_build_codebook(df_histogram(kind, a), max_len))
+
+
+# ----------------------------------------------------------------- device API
+class DeviceContainer:
+    """A container's sections copied to device memory (torch uint8 tensors)
+    and the df_device_view that borrows them."""
+
+    def __init__(self, c: Container, device="cuda"):
+        inf = c.info()
+        self.kind = int(inf["kind"])
+        self.n = int(inf["n"])
+        self.info = inf
+        self.device = torch.device(device)
+        self.sections = {}
+        for i, name in enumerate(SECTION_NAMES):
+            host = np.asarray(c.section(i)).view(np.uint8)
+            t = torch.empty(max(host.size, 16), dtype=torch.uint8, device=self.device)
+            if host.size:
+                t[: host.size].copy_(torch.from_numpy(np.array(host)), non_blocking=False)
+            self.sections[name] = t
+        v = df_device_view()
+        v.kind = self.kind
+        v.n_luts = inf["n_luts"]
+        v.max_tile_elems = inf["max_tile_elems"]
+        v.n = inf["n"]
+        v.total_bits = inf["total_bits"]
+        v.n_threads = inf["n_threads"]
+        v.n_tiles = inf["n_tiles"]
+        v.bitstream = self.sections["bitstream"].data_ptr()
+        v.gaps = self.sections["gaps"].data_ptr()
+        v.tile_out = self.sections["tile_out"].data_ptr()
+        v.sign_mantissa = self.sections["sign_mantissa"].data_ptr() if self.kind == KIND_BF16 else None
+        v.lut = self.sections["lut"].data_ptr()
+        v.dtab = self.sections["dtab"].data_ptr()
+        self.view = v
+
+    def compressed_bytes(self) -> int:
+        """Bytes of the stored sections (every section but the derived DTAB)."""
+        return sum(v for k, v in self.info["section_bytes"].items() if k != "dtab")
+
+    def empty_output(self) -> torch.Tensor:
+        dt = torch.bfloat16 if self.kind == KIND_BF16 else torch.uint8
+        return torch.empty(self.n, dtype=dt, device=self.device)
+
+
+def to_device(c: Container, device="cuda") -> DeviceContainer:
+    return DeviceContainer(c, device)
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check_dst(dc: DeviceContainer, dst: torch.Tensor):
+    need = dc.n * (2 if dc.kind == KIND_BF16 else 1)
+    if not dst.is_cuda or not dst.is_contiguous() or dst.numel() * dst.element_size() < need:
+        raise ValueError("dst must be a contiguous device tensor of at least %d bytes" % need)
+
+
+def df_decompress(dc: DeviceContainer, dst: torch.Tensor, stream=None):
+    _check_dst(dc, dst)
+    _check(lib().df_decompress(ctypes.byref(dc.view), ctypes.c_void_p(dst.data_ptr()),
+                               _stream_handle(stream, dst.device)), "df_decompress")
+
+
+def df_decompress_checked(dc: DeviceContainer, dst: torch.Tensor, err: torch.Tensor, stream=None):
+    """err: a device int32/uint32 tensor of one element, zeroed by the caller."""
+    _check_dst(dc, dst)
+    if not err.is_cuda or err.element_size() != 4:
+        raise ValueError("err must be a 4-byte device tensor")
+    _check(lib().df_decompress_checked(ctypes.byref(dc.view), ctypes.c_void_p(dst.data_ptr()),
+                                       ctypes.c_void_p(err.data_ptr()),
+                                       _stream_handle(stream, dst.device)), "df_decompress_checked")
+
+
+def df_decompress_batch(dcs, dsts, stream=None):
+    if len(dcs) != len(dsts):
+        raise ValueError("one destination per container")
+    for dc, d in zip(dcs, dsts):
+        _check_dst(dc, d)
+    views = (df_device_view * max(len(dcs), 1))(*[dc.view for dc in dcs])
+    ptrs = (ctypes.c_void_p * max(len(dsts), 1))(*[d.data_ptr() for d in dsts])
+    dev = dsts[0].device if dsts else None
+    _check(lib().df_decompress_batch(views, ptrs, len(dcs), _stream_handle(stream, dev)),
+           "df_decompress_batch")

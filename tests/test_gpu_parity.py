@@ -1,0 +1,278 @@
+"""GPU parity: the HIP decoder against the definition of the result
+(decode(encode(x)) == x, bit for bit) and against the CPU oracle's own
+decode of the same container.  Bit-exact (0 ULP) everywhere: this is
+integer work.  Every call goes through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_huffman_amd as dfh
+from lossless_entropy_coded_huffman_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+EDGE_SIZES = [1, 2, 63, 64, 65, 255, 256, 257, 6143, 16384, 16385, 100_003, 1_000_001]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, torch.device("cuda:0")
+
+
+def host_of(t, kind):
+    import torch
+    a = t.view(torch.int16) if kind == 0 else t
+    a = a.cpu().numpy()
+    return a.view(np.uint16) if kind == 0 else a
+
+
+def gpu_decode(torch_dev, c, checked=True):
+    torch, dev = torch_dev
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    if checked:
+        dfh.df_decompress_checked(dc, out, err)
+    else:
+        dfh.df_decompress(dc, out)
+    torch.cuda.synchronize()
+    return host_of(out, dc.kind), int(err.item())
+
+
+def oracle_container(c):
+    inf = c.info()
+    d = {k: np.asarray(c.section(k)) for k in dfh.SECTION_NAMES}
+    d.update(kind=inf["kind"], n=inf["n"], n_tiles=inf["n_tiles"], n_threads=inf["n_threads"],
+             lengths=inf["lengths"])
+    return d
+
+
+def check(torch_dev, orc, kind, src, checked=True, oracle_threads=8):
+    c = dfh.compress(kind, src)
+    got, err = gpu_decode(torch_dev, c, checked)
+    assert err == 0
+    assert np.array_equal(got, src)
+    ref = orc.decode_tiles(oracle_container(c), oracle_threads)
+    assert np.array_equal(got, ref)
+    return c
+
+
+def bf16_normal(n, seed, std=0.02):
+    return synth.bf16_rne(np.random.default_rng(seed).normal(0, std, n).astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_c1_tensor(torch_dev, orc, seed):
+    say("c1 seed", seed)
+    check(torch_dev, orc, 0, synth.c1_tensor(seed))
+
+
+@pytest.mark.parametrize("n", EDGE_SIZES)
+@pytest.mark.parametrize("kind", [0, 1])
+def test_edge_sizes(torch_dev, orc, kind, n):
+    say("edge", kind, n)
+    if kind == 0:
+        src = bf16_normal(n, n)
+    else:
+        src = synth.quantize_u8(np.random.default_rng(n).normal(0, 1, n).astype(np.float32), n % 2 == 1)
+    check(torch_dev, orc, kind, src)
+
+
+def test_unchecked_equals_checked(torch_dev, orc):
+    src = bf16_normal(3_000_000, 7)
+    c = dfh.compress(0, src)
+    a, _ = gpu_decode(torch_dev, c, checked=False)
+    b, err = gpu_decode(torch_dev, c, checked=True)
+    assert err == 0 and np.array_equal(a, src) and np.array_equal(b, src)
+
+
+def test_empty(torch_dev):
+    torch, dev = torch_dev
+    for kind in (0, 1):
+        c = dfh.compress(kind, np.zeros(0, np.uint16 if kind == 0 else np.uint8))
+        dc = dfh.to_device(c, dev)
+        out = torch.empty(16, dtype=torch.uint8, device=dev)
+        dfh.df_decompress(dc, out)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [1, 64, 65, 16384, 16385, 40000])
+def test_single_symbol(torch_dev, orc, n):
+    say("single symbol", n)
+    check(torch_dev, orc, 0, np.full(n, 0xBC00, np.uint16))
+    check(torch_dev, orc, 1, np.full(n, 77, np.uint8))
+
+
+def test_all_bf16_patterns(torch_dev, orc):
+    u = np.random.default_rng(11).permutation(65536).astype(np.uint16)
+    check(torch_dev, orc, 0, np.concatenate([u, u[::-1], u]))
+
+
+def test_stream_ends_on_chunk_and_tile_boundaries(torch_dev, orc):
+    # 256 equal counts give 8-bit codes: total bits = 8 n
+    for n in (8, 2048, 4096, 2048 * 7):
+        src = np.tile(np.arange(256, dtype=np.uint8), n // 256 + 1)[:n]
+        if n < 256:
+            continue
+        c = check(torch_dev, orc, 1, src)
+        assert c.info()["total_bits"] % 64 == 0
+
+
+def test_codes_of_every_length_up_to_32(torch_dev, orc):
+    # lengths 1, 2, ..., 32, 32 (Kraft sum exactly 1): symbols drawn uniformly,
+    # so codes of 25-32 bits (four table levels) are frequent and straddle
+    # chunk and tile ends
+    ln = np.zeros(256, np.uint8)
+    syms = np.arange(40, 73)
+    ln[syms] = list(range(1, 33)) + [32]
+    rng = np.random.default_rng(5)
+    for kind in (0, 1):
+        s = rng.choice(syms, 300_000).astype(np.uint8)
+        if kind == 0:
+            src = (s.astype(np.uint16) << 7) | rng.integers(0, 2, s.size).astype(np.uint16) << 15 \
+                | rng.integers(0, 128, s.size).astype(np.uint16)
+        else:
+            src = s
+        c = dfh.df_encode(kind, src, ln)
+        assert c.info()["n_luts"] >= 4
+        got, err = gpu_decode(torch_dev, c)
+        assert err == 0 and np.array_equal(got, src)
+        assert np.array_equal(got, orc.decode_tiles(oracle_container(c), 8))
+
+
+def test_heavy_tail_t3(torch_dev, orc):
+    src = synth.bf16_rne((np.random.default_rng(3).standard_t(3, 4_000_000) * 0.02 / np.sqrt(3))
+                         .astype(np.float32))
+    c = check(torch_dev, orc, 0, src)
+    assert c.info()["lengths"].max() > 12
+
+
+def test_u8_entrollm_layers(torch_dev, orc):
+    layers = synth.u8_block(0, shapes=synth.scaled_shapes(synth.LLAMA3_8B_BLOCK, 8))
+    for name, q, asym in layers:
+        say("u8 layer", name, q.size, asym)
+        check(torch_dev, orc, 1, q)
+
+
+def test_batch_matches_single(torch_dev, orc):
+    torch, dev = torch_dev
+    for kind in (0, 1):
+        srcs = []
+        for i, n in enumerate([1, 5000, 700_001, 65, 3_000_000]):
+            if kind == 0:
+                srcs.append(bf16_normal(n, 40 + i, 0.01 * (i + 1)))
+            else:
+                srcs.append(synth.quantize_u8(np.random.default_rng(i).normal(0, 1, n).astype(np.float32), i % 2 == 0))
+        cs = [dfh.compress(kind, s) for s in srcs]
+        dcs = [dfh.to_device(c, dev) for c in cs]
+        outs = [dc.empty_output() for dc in dcs]
+        dfh.df_decompress_batch(dcs, outs)
+        torch.cuda.synchronize()
+        for s, o in zip(srcs, outs):
+            assert np.array_equal(host_of(o, kind), s)
+
+
+def test_batch_more_than_16(torch_dev):
+    torch, dev = torch_dev
+    srcs = [bf16_normal(10_000 + 977 * i, 90 + i) for i in range(21)]
+    dcs = [dfh.to_device(dfh.compress(0, s), dev) for s in srcs]
+    outs = [dc.empty_output() for dc in dcs]
+    dfh.df_decompress_batch(dcs, outs)
+    torch.cuda.synchronize()
+    for s, o in zip(srcs, outs):
+        assert np.array_equal(host_of(o, 0), s)
+
+
+def test_no_writes_outside_dst(torch_dev):
+    torch, dev = torch_dev
+    for kind, n in ((0, 100_003), (1, 100_003), (0, 17), (1, 33)):
+        src = bf16_normal(n, 1) if kind == 0 else np.random.default_rng(2).integers(0, 40, n).astype(np.uint8)
+        dc = dfh.to_device(dfh.compress(kind, src), dev)
+        esz = 2 if kind == 0 else 1
+        guard = 4096
+        buf = torch.full((guard * 2 + n * esz + 16,), 0xA5, dtype=torch.uint8, device=dev)
+        dst = buf[guard: guard + n * esz]
+        dfh.df_decompress(dc, dst)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy()
+        assert (b[:guard] == 0xA5).all() and (b[guard + n * esz:] == 0xA5).all()
+        got = b[guard: guard + n * esz].view(np.uint16 if kind == 0 else np.uint8)
+        assert np.array_equal(got, src)
+
+
+def test_checked_reports_bad_tile_offsets(torch_dev):
+    # error path forced from the host: a tile offset edited on the device;
+    # the kernel clamps every access and exits normally, reporting the count
+    # mismatch
+    torch, dev = torch_dev
+    src = bf16_normal(500_000, 4)
+    dc = dfh.to_device(dfh.compress(0, src), dev)
+    to = dc.sections["tile_out"].view(torch.int64)
+    to[1] += 1
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dfh.df_decompress_checked(dc, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & dfh.DEVERR_COUNT
+
+
+def test_rejects_bad_arguments(torch_dev):
+    torch, dev = torch_dev
+    dc = dfh.to_device(dfh.compress(0, bf16_normal(1000, 1)), dev)
+    out = torch.empty(1000 * 2 + 16, dtype=torch.uint8, device=dev)
+    with pytest.raises(dfh.DFError):
+        dfh.df_decompress(dc, out[1:1 + 2000])      # misaligned destination
+    dc.view.n_luts = 0
+    with pytest.raises(dfh.DFError):
+        dfh.df_decompress(dc, out)
+
+
+# ------------------------------------------------------------ full-size cases
+def test_llama3_8b_block_bf16(torch_dev, orc):
+    """One Llama-3-8B-shaped block (218,103,808 BF16 weights), one codebook,
+    one launch -- the benchmark's workload and launch."""
+    torch, dev = torch_dev
+    say("8B block: generate")
+    src, _ = synth.bf16_block(0)
+    say("8B block: compress")
+    c = dfh.compress(0, src)
+    inf = c.info()
+    say("8B block:", {k: inf[k] for k in ("n", "total_bits", "n_tiles", "n_luts", "max_tile_elems")})
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dfh.df_decompress_checked(dc, out, err)
+    dfh.df_decompress(dc, out)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = torch.from_numpy(src.view(np.int16)).to(dev)
+    assert torch.equal(out.view(torch.int16), ref)
+    say("8B block: oracle decode")
+    got = host_of(out, 0)
+    assert np.array_equal(got, orc.decode_tiles(oracle_container(c), 16))
+
+
+def test_llama3_8b_block_u8(torch_dev, orc):
+    """The EntroLLM-style block: seven per-layer uint8 containers, one batched
+    launch."""
+    torch, dev = torch_dev
+    layers = synth.u8_block(0)
+    cs = [dfh.compress(1, q) for _, q, _ in layers]
+    dcs = [dfh.to_device(c, dev) for c in cs]
+    outs = [dc.empty_output() for dc in dcs]
+    dfh.df_decompress_batch(dcs, outs)
+    torch.cuda.synchronize()
+    for (name, q, _), c, o in zip(layers, cs, outs):
+        say("u8 layer", name)
+        assert torch.equal(o, torch.from_numpy(q).to(dev))
+    got = host_of(outs[4], 1)
+    assert np.array_equal(got, orc.decode_tiles(oracle_container(cs[4]), 16))

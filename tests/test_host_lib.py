@@ -1,0 +1,202 @@
+"""Host half of the product library (C ABI through the ctypes binding) against
+the CPU oracle: same histograms, same code lengths, byte-identical sections,
+decode tables that the oracle's checker accepts, cross-decoding, container
+files and validation.  No GPU needed."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lossless_entropy_coded_huffman_amd as dfh
+from lossless_entropy_coded_huffman_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SECTIONS = ["bitstream", "gaps", "tile_out", "sign_mantissa", "lut"]
+EDGE_SIZES = [0, 1, 2, 63, 64, 65, 255, 256, 257, 6143, 16384, 16385, 100_003]
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dfh.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(df_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert "df_decompress" in names and "df_encode" in names and len(names) >= 13
+    L = dfh.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def inputs(kind, n, seed, dist="normal"):
+    rng = np.random.default_rng(seed)
+    if kind == dfh.KIND_BF16:
+        x = rng.standard_t(3, n) * 0.02 if dist == "t3" else rng.normal(0, 0.02, n)
+        return synth.bf16_rne(x.astype(np.float32))
+    return synth.quantize_u8(rng.normal(0, 0.02, n).astype(np.float32), bool(seed & 1))
+
+
+def lib_sections(c):
+    return {k: np.asarray(c.section(k)) for k in dfh.SECTION_NAMES}
+
+
+def as_oracle_container(c):
+    inf = c.info()
+    d = lib_sections(c)
+    d.update(kind=inf["kind"], n=inf["n"], n_tiles=inf["n_tiles"], n_threads=inf["n_threads"],
+             lengths=inf["lengths"])
+    return d
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("n", EDGE_SIZES)
+def test_sections_identical_to_oracle(orc, kind, n):
+    src = inputs(kind, n, n + kind)
+    h = dfh.df_histogram(kind, src)
+    assert np.array_equal(h, orc.histogram(kind, src))
+    ln = dfh.df_build_codebook(h)
+    assert np.array_equal(ln, orc.code_lengths(h))
+    c = dfh.df_encode(kind, src, ln)
+    o = orc.encode(kind, src, ln)
+    o["lut"], o["n_luts"] = orc.build_lut(ln)
+    inf = c.info()
+    for k in ("n", "total_bits", "n_threads", "n_tiles", "max_tile_elems", "n_luts"):
+        assert inf[k] == o[k], k
+    got = lib_sections(c)
+    for k in SECTIONS:
+        if k == "sign_mantissa" and kind == 1:
+            assert got[k].size == 0
+            continue
+        assert np.array_equal(got[k], o[k]), k
+    assert orc.check_dtab(kind, ln, got["dtab"]) == 0
+    c.validate()
+    assert np.array_equal(orc.decode_tiles(as_oracle_container(c), 4), src)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_codebook_matches_oracle_random(orc, seed):
+    rng = np.random.default_rng(1000 + seed)
+    h = np.zeros(256, np.uint64)
+    m = int(rng.integers(1, 257))
+    h[rng.choice(256, m, replace=False)] = (rng.pareto(0.7, m) * 10 + 1).astype(np.uint64)
+    assert np.array_equal(dfh.df_build_codebook(h), orc.code_lengths(h))
+    for L in (12, 16, 24):
+        if m <= 2 ** L:
+            assert np.array_equal(dfh.df_build_codebook(h, L), orc.code_lengths(h, L))
+
+
+def test_codebook_length_limited_fibonacci(orc):
+    fib = [1, 1]
+    while len(fib) < 40:
+        fib.append(fib[-1] + fib[-2])
+    h = np.zeros(256, np.uint64)
+    h[100:140] = fib
+    ln = dfh.df_build_codebook(h)
+    assert ln.max() == 32
+    assert np.array_equal(ln, orc.code_lengths(h))
+
+
+def test_codebook_errors():
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_build_codebook(np.ones(256, np.uint64), 7)
+    assert e.value.status == -3
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_build_codebook(np.ones(256, np.uint64), 33)
+    assert e.value.status == -1
+
+
+def test_encode_rejects_symbol_without_code():
+    src = np.array([1, 2, 3], np.uint8)
+    ln = np.zeros(256, np.uint8)
+    ln[1] = ln[2] = 1
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_encode(dfh.KIND_U8, src, ln)
+    assert e.value.status == -3
+
+
+def test_encode_rejects_kraft_violation():
+    ln = np.zeros(256, np.uint8)
+    ln[:3] = 1
+    with pytest.raises(dfh.DFError):
+        dfh.df_encode(dfh.KIND_U8, np.zeros(4, np.uint8), ln)
+
+
+def test_all_bf16_patterns(orc):
+    u = np.random.default_rng(3).permutation(65536).astype(np.uint16)
+    c = dfh.compress(dfh.KIND_BF16, u)
+    o = orc.compress(dfh.KIND_BF16, u)
+    for k in SECTIONS:
+        assert np.array_equal(np.asarray(c.section(k)), o[k]), k
+    assert np.array_equal(orc.decode_tiles(as_oracle_container(c), 2), u)
+
+
+def test_heavy_tail_reaches_long_codes(orc):
+    src = inputs(0, 2_000_000, 5, "t3")
+    c = dfh.compress(0, src)
+    inf = c.info()
+    assert inf["lengths"].max() > 12          # exercises the long-code path
+    o = orc.compress(0, src)
+    for k in SECTIONS:
+        assert np.array_equal(np.asarray(c.section(k)), o[k]), k
+
+
+def test_save_load_round_trip(tmp_path):
+    src = inputs(0, 50_000, 9)
+    c = dfh.compress(0, src)
+    p = str(tmp_path / "c.dfh")
+    c.save(p)
+    c2 = dfh.df_container_load(p)
+    for k in dfh.SECTION_NAMES:
+        assert np.array_equal(np.asarray(c.section(k)), np.asarray(c2.section(k))), k
+    assert c.info()["total_bits"] == c2.info()["total_bits"]
+
+
+def test_load_rejects_corrupt_files(tmp_path):
+    src = inputs(1, 40_000, 4)
+    c = dfh.compress(1, src)
+    p = str(tmp_path / "c.dfh")
+    c.save(p)
+    raw = bytearray(open(p, "rb").read())
+    # bad magic
+    bad = bytearray(raw)
+    bad[0] ^= 0xFF
+    open(p + ".1", "wb").write(bad)
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_container_load(p + ".1")
+    assert e.value.status == -4
+    # truncated
+    open(p + ".2", "wb").write(raw[: len(raw) // 2])
+    with pytest.raises(dfh.DFError):
+        dfh.df_container_load(p + ".2")
+    # tile_out edited: find the tile_out section (third stored section)
+    inf = c.info()
+    sb = inf["section_bytes"]
+    off = 64 + 256
+    for name in ("bitstream", "gaps"):
+        off += 64 + (sb[name] + 63) // 64 * 64
+    off += 64
+    bad = bytearray(raw)
+    bad[off + 8: off + 16] = (inf["n"] + 5).to_bytes(8, "little")   # tile_out[1] > n
+    open(p + ".3", "wb").write(bad)
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_container_load(p + ".3")
+    assert e.value.status == -6
+    # a length byte changed: Kraft no longer holds
+    bad = bytearray(raw)
+    first_used = 64 + int(np.nonzero(inf["lengths"])[0][0])
+    bad[first_used] += 1
+    open(p + ".4", "wb").write(bad)
+    with pytest.raises(dfh.DFError):
+        dfh.df_container_load(p + ".4")
+
+
+def test_one_symbol_and_empty(orc):
+    src = np.full(70_000, 0x3F80, np.uint16)
+    c = dfh.compress(0, src)
+    assert c.info()["total_bits"] == 70_000
+    assert np.array_equal(orc.decode_tiles(as_oracle_container(c), 3), src)
+    assert orc.check_dtab(0, c.info()["lengths"], np.asarray(c.section("dtab"))) == 0
+    e = dfh.compress(1, np.zeros(0, np.uint8))
+    assert e.info()["n_tiles"] == 0 and list(np.asarray(e.section("tile_out"))) == [0]
