@@ -124,6 +124,9 @@ def main():
                     choices=["llama3_8b_block_bf16", "c1_1m_bf16", "llama3_8b_block_u8",
                              "llama31_405b_block_t3_bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the codec, time a plain device copy of MIB MiB (the "
+                         "reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the codec needs no collectives and this build "
@@ -140,6 +143,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU")
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args)
+        return
 
     log("workload", args.workload, "seed", args.seed)
     kind, srcs, wconf = make_workload(args.workload, args.seed)
@@ -221,6 +227,23 @@ def main():
     print(json.dumps(line), flush=True)
     if not verified:
         sys.exit(1)
+
+
+def copy_calibration(torch, dev, args):
+    nbytes = args.copy_calibration << 20
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "ms_per_copy": round(dt * 1e3, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
 def kernel_sha() -> str:

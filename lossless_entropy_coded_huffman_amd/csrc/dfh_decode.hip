@@ -13,21 +13,28 @@
 // live in on-chip memory.  Section "Descompressao por bloco de transformer":
 // a whole block of matrices is one launch.
 //
-// The gfx950 design (one workgroup = 256 lanes = 4 wave64):
-//   - persistent workgroups: each stages its container's tables in LDS once
-//     (the 4096-entry multi-code table, 32 KiB, and the hierarchical tables,
-//     512 B each) and then loops over tiles;
-//   - a lane keeps its 8 stream bytes plus the next 4 in three registers
-//     (12-byte window) loaded straight from HBM, so the stream is read once;
+// The gfx950 design:
+//   - a tile (the pages' thread block: 256 threads x 8 stream bytes) is
+//     decoded by a group of 256 lanes (4 wave64); a workgroup runs up to four
+//     such groups, so four tiles share one copy of the tables in LDS (the
+//     4096-entry multi-code table, 32 KiB, then the hierarchical tables,
+//     512 B each), which lets two 1024-lane workgroups share a CU;
+//   - workgroups are persistent and walk the container in steps of
+//     (groups x workgroups) tiles; while a step decodes, the next step's
+//     stream words, gap fields and tile offsets are already in flight, and
+//     the current tile's sign|mantissa bytes are requested before decoding
+//     starts, so HBM latency overlaps the decode;
+//   - a lane keeps its 8 stream bytes plus the next 4 in three registers; the
+//     decode loops are split at bit 32 so that a 32-bit window is one
+//     funnel shift of a fixed register pair;
 //   - a lookup in the multi-code table yields up to five codes; codes longer
 //     than 12 bits fall back to the hierarchical tables;
-//   - the block prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus one
-//     LDS step across the four waves;
-//   - phase 2 ORs the decoded bytes into an LDS staging buffer laid out so
-//     that its byte j holds output element (tile start rounded down to the
-//     16-byte store granule) + j; the store pass then reads aligned LDS
-//     words, merges the sign|mantissa bytes (BF16) and issues 16-byte
-//     global stores.
+//   - the per-tile prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus
+//     one LDS step across the group's four waves;
+//   - phase 2 ORs the decoded bytes into the group's LDS staging buffer,
+//     whose byte j holds output element (tile start rounded down to the
+//     store granule) + j; the store pass reads aligned LDS words, merges the
+//     sign|mantissa bytes (BF16) and issues 16-byte global stores.
 
 #include <hip/hip_runtime.h>
 
@@ -38,10 +45,12 @@
 
 namespace {
 
-constexpr uint32_t kTPB = DF_THREADS_PER_TILE;  // lanes per workgroup = threads per tile
+constexpr uint32_t kTPB = DF_THREADS_PER_TILE;  // lanes per tile group = threads per tile
+constexpr uint32_t kMaxGroups = 4;              // tile groups per workgroup
 constexpr uint32_t kK = DF_DTAB_BITS;           // multi-code table index width
 constexpr uint32_t kDtabEntries = 1u << kK;
 constexpr uint32_t kDtabBytes = kDtabEntries * 8;
+constexpr uint32_t kPrefetch = 4;  // sign|mantissa 8-byte groups requested ahead per lane
 
 struct Job {
   const uint32_t *bits;  // bitstream, little-endian 32-bit words
@@ -58,8 +67,10 @@ struct Job {
 struct Batch {
   Job job[DF_MAX_BATCH];
   uint32_t count;
-  uint32_t lds_out_bytes;  // output staging area at the start of LDS
-  uint32_t *err;           // error word (checked launches only)
+  uint32_t lut_bytes;  // LDS reserved for hierarchical tables
+  uint32_t out_bytes;  // LDS staging bytes per tile group
+  uint32_t pad;
+  uint32_t *err;       // error word (checked launches only)
 };
 
 // Stream bits [p, p + 32) of the 96-bit window w2:w1:w0, for p < 64.
@@ -70,12 +81,17 @@ __device__ __forceinline__ uint32_t window(uint32_t w0, uint32_t w1, uint32_t w2
   return (uint32_t)((((uint64_t)hi << 32) | lo) >> (p & 31));
 }
 
+// Bits [s, s + 32) of hi:lo, s taken mod 32 (v_alignbit_b32).
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t s) {
+  return (uint32_t)((((uint64_t)hi << 32) | lo) >> (s & 31));
+}
+
 // One code through the hierarchical tables: returns (length << 8) | symbol.
 // A prefix with no code (possible only for an incomplete code or a corrupt
 // stream) reports DF_DEVERR_CODE in checked launches and consumes one bit.
 template <bool CHECKED>
 __device__ __forceinline__ uint32_t long_code(const uint16_t *lut, uint32_t n_luts, uint32_t win,
-                                           uint32_t *err) {
+                                              uint32_t *err) {
   uint32_t e = lut[win & 255];
   uint32_t sh = 8;
   for (int d = 0; d < 3 && (e & 0x8000u); d++) {
@@ -106,19 +122,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix sum over the 256 lanes; *total gets the sum.  Contains a
-// barrier.
-__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *wsum, uint32_t *total) {
-  const uint32_t lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const uint32_t x = wave_inclusive_sum(v);
-  if (lane == 63) wsum[wid] = x;
-  __syncthreads();
-  const uint32_t s0 = wsum[0], s1 = wsum[1], s2 = wsum[2], s3 = wsum[3];
-  *total = s0 + s1 + s2 + s3;
-  const uint32_t before = (wid > 0 ? s0 : 0u) + (wid > 1 ? s1 : 0u) + (wid > 2 ? s2 : 0u);
-  return before + x - v;
-}
-
 // OR up to five symbol bytes (s0 = bytes 0..3, s1 = byte 4) into the staging
 // buffer at byte q; they span at most two aligned words.
 __device__ __forceinline__ void put_bytes(uint8_t *out, uint32_t q, uint32_t qmax, uint32_t s0,
@@ -141,174 +144,277 @@ __device__ __forceinline__ uint2 merge4(uint32_t e4, uint32_t s4) {
   return make_uint2((x0 & 0x7F7F7F7Fu) | (y0 & 0x80808080u), (x1 & 0x7F7F7F7Fu) | (y1 & 0x80808080u));
 }
 
+// Phase-1 lookup: counts the codes of one table entry, returns bits used.
+template <bool CHECKED>
+__device__ __forceinline__ uint32_t count_step(const uint32_t *dtw, const uint16_t *lut, uint32_t n_luts,
+                                               uint32_t win, uint32_t *err, uint32_t &cnt) {
+  const uint32_t h = dtw[((win & (kDtabEntries - 1)) << 1) | 1];
+  uint32_t adv = (h >> 24) & 15;
+  uint32_t nc = h >> 28;
+  if (adv == 0) {
+    adv = long_code<CHECKED>(lut, n_luts, win, err) >> 8;
+    nc = 1;
+  }
+  cnt += nc;
+  return adv;
+}
+
+// Phase-1 lookup near the chunk end: only codes starting before bit r of the
+// window count (1 <= r <= 12).
+template <bool CHECKED>
+__device__ __forceinline__ uint32_t count_step_clip(const uint32_t *dtw, const uint16_t *lut,
+                                                    uint32_t n_luts, uint32_t win, uint32_t r,
+                                                    uint32_t *err, uint32_t &cnt) {
+  const uint32_t h = dtw[((win & (kDtabEntries - 1)) << 1) | 1];
+  uint32_t adv = (h >> 24) & 15;
+  uint32_t starts = (h >> 8) & 0xFFFu;
+  if (adv == 0) {
+    adv = long_code<CHECKED>(lut, n_luts, win, err) >> 8;
+    starts = 1;
+  }
+  cnt += __popc(starts & ((1u << r) - 1));
+  return adv;
+}
+
+// Phase-2 lookup: writes the entry's symbol bytes at q, returns bits used.
+// CLIP: keep only codes starting before bit r of the window.
+template <int KIND, bool CHECKED, bool CLIP>
+__device__ __forceinline__ uint32_t decode_step(const uint64_t *dtab, const uint16_t *lut,
+                                                uint32_t n_luts, uint32_t win, uint32_t r, uint32_t *err,
+                                                uint8_t *out, uint32_t &q, uint32_t qmax) {
+  const uint2 e = *(const uint2 *)(dtab + (win & (kDtabEntries - 1)));
+  uint32_t adv = (e.y >> 24) & 15;
+  uint32_t nc = e.y >> 28;
+  uint32_t s0 = e.x, s1 = e.y & 0xFFu;
+  uint32_t starts = (e.y >> 8) & 0xFFFu;
+  if (adv == 0) {
+    const uint32_t c = long_code<CHECKED>(lut, n_luts, win, err);
+    adv = c >> 8;
+    s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+    s1 = 0;
+    nc = 1;
+    starts = 1;
+  }
+  if (CLIP) {
+    nc = __popc(starts & ((1u << r) - 1));
+    if (nc < 5) {
+      s1 = 0;
+      if (nc < 4) s0 &= (1u << (8 * nc)) - 1;
+    }
+  }
+  put_bytes(out, q, qmax, s0, s1);
+  q += nc;
+  return adv;
+}
+
+// Element-wise stores of the part of a 16-byte store granule that lies in
+// [lo, hi) (granules shared with a neighbouring tile).
+__device__ __forceinline__ void store_partial(uint16_t *dst, uint32_t e0, uint32_t lo, uint32_t hi, uint4 o) {
+#pragma unroll
+  for (uint32_t i = 0; i < 8; i++) {
+    const uint32_t w = i < 2 ? o.x : i < 4 ? o.y : i < 6 ? o.z : o.w;
+    if (e0 + i >= lo && e0 + i < hi) dst[e0 + i] = (uint16_t)(w >> (16 * (i & 1)));
+  }
+}
+
+__device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_t lo, uint32_t hi, uint4 o) {
+#pragma unroll
+  for (uint32_t i = 0; i < 16; i++) {
+    const uint32_t w = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
+    if (e0 + i >= lo && e0 + i < hi) dst[e0 + i] = (uint8_t)(w >> (8 * (i & 3)));
+  }
+}
+
+struct ChunkRegs {
+  uint32_t w0, w1, w2, g0, g1;
+};
+
+// The stream words and gap fields of one lane of a tile.  Addresses are a
+// wave-uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, uint32_t lane) {
+  ChunkRegs c = {0u, 0u, 0u, 0u, 0u};
+  if (tile < jb.n_tiles) {
+    const uint32_t *bits_t = jb.bits + tile * (2 * kTPB);
+    const uint2 w01 = *(const uint2 *)(bits_t + 2 * lane);
+    c.w0 = w01.x;
+    c.w1 = w01.y;
+    c.w2 = bits_t[2 * lane + 2];
+    const uint32_t *gaps_t = jb.gaps + tile * (5 * kTPB / 32);  // 1280 bits per tile
+    c.g0 = gaps_t[(5 * lane) >> 5];
+    c.g1 = gaps_t[((5 * lane) >> 5) + 1];
+  }
+  return c;
+}
+
 template <int KIND, bool CHECKED>
-__global__ __launch_bounds__(256) void decode_kernel(const Batch batch) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
+void decode_kernel(const Batch batch) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wsum[4 * kMaxGroups];
 
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
   const Job &jb = batch.job[j];
   const uint32_t tid = threadIdx.x;
-
-  uint8_t *out_lds = smem;
-  const uint32_t lds_out_bytes = batch.lds_out_bytes;
-  uint64_t *dtab_lds = (uint64_t *)(smem + lds_out_bytes);
-  uint16_t *lut_lds = (uint16_t *)(smem + lds_out_bytes + kDtabBytes);
+  const uint32_t groups = blockDim.x / kTPB;
+  const uint32_t grp = __builtin_amdgcn_readfirstlane(tid / kTPB);
+  const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
+
+  uint64_t *dtab_lds = (uint64_t *)smem;
+  const uint32_t *dtw = (const uint32_t *)smem;
+  uint16_t *lut_lds = (uint16_t *)(smem + kDtabBytes);
+  uint8_t *out_lds = smem + kDtabBytes + batch.lut_bytes + grp * batch.out_bytes;
+  const uint32_t qmax = batch.out_bytes - 8;
 
   {  // stage the tables once per workgroup
     const uint4 *src = (const uint4 *)jb.dtab;
     uint4 *dl = (uint4 *)dtab_lds;
-    for (uint32_t i = tid; i < kDtabBytes / 16; i += kTPB) dl[i] = src[i];
+    for (uint32_t i = tid; i < kDtabBytes / 16; i += blockDim.x) dl[i] = src[i];
     const uint4 *ls = (const uint4 *)jb.lut;
     uint4 *ll = (uint4 *)lut_lds;
-    for (uint32_t i = tid; i < n_luts * 32; i += kTPB) ll[i] = ls[i];
+    for (uint32_t i = tid; i < n_luts * 32; i += blockDim.x) ll[i] = ls[i];
+  }
+
+  const uint64_t step = (uint64_t)jb.wg_count * groups;
+  uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
+  ChunkRegs nxt = load_chunk(jb, base + grp, lane);
+  uint64_t nlo = 0, nhi = 0;
+  if (base + grp < jb.n_tiles) {
+    nlo = jb.tile_out[base + grp];
+    nhi = jb.tile_out[base + grp + 1];
   }
   __syncthreads();
 
-  const uint32_t *dtab_words = (const uint32_t *)dtab_lds;
-  const uint32_t qmax = lds_out_bytes - 8;
-
-  for (uint64_t tile = wg - jb.wg_begin; tile < jb.n_tiles; tile += jb.wg_count) {
-    uint64_t lo = jb.tile_out[tile];
-    uint64_t hi = jb.tile_out[tile + 1];
+  for (; base < jb.n_tiles; base += step) {
+    const uint64_t tile = base + grp;  // wave-uniform
+    const bool active = tile < jb.n_tiles;
+    const ChunkRegs cur = nxt;
+    uint64_t lo = nlo, hi = nhi;
+    // next step's stream words, gaps and offsets go in flight now
+    nxt = load_chunk(jb, tile + step, lane);
+    if (tile + step < jb.n_tiles) {
+      nlo = jb.tile_out[tile + step];
+      nhi = jb.tile_out[tile + step + 1];
+    }
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
     if (hi - lo > jb.max_tile_elems) hi = lo + jb.max_tile_elems;
+    // output range relative to the store-granule-aligned base a
     const uint64_t a = KIND == DF_KIND_BF16 ? (lo & ~7ull) : (lo & ~15ull);
+    const uint32_t lo_r = (uint32_t)(lo - a), hi_r = (uint32_t)(hi - a);
+    const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : 16u;  // elements per store granule
+    const uint32_t ngroups = active ? (hi_r + gsz - 1) / gsz : 0u;
 
-    // this lane's chunk: stream bits [64T, 64T + 96) and its gap
-    const uint64_t T = tile * kTPB + tid;
-    const uint2 w01 = *(const uint2 *)(jb.bits + 2 * T);
-    const uint32_t w0 = w01.x, w1 = w01.y, w2 = jb.bits[2 * T + 2];
+    // this tile's sign|mantissa bytes go in flight before decoding
+    uint2 smv[kPrefetch];
+    const uint8_t *sm_t = jb.sm + a;
+    if (KIND == DF_KIND_BF16) {
+#pragma unroll
+      for (uint32_t k = 0; k < kPrefetch; k++) {
+        const uint32_t g = lane + k * kTPB;
+        smv[k] = g < ngroups ? *(const uint2 *)(sm_t + 8 * g) : make_uint2(0, 0);
+      }
+    }
+
+    // chunk bounds: codes start in [gap, E) of this lane's 64 stream bits
     uint32_t gap = 0, E = 0;
-    if (T < jb.n_threads) {
-      const uint64_t gb = 5 * T;
-      const uint32_t g0 = jb.gaps[gb >> 5], g1 = jb.gaps[(gb >> 5) + 1];
-      gap = (uint32_t)(((((uint64_t)g1) << 32) | g0) >> (gb & 31)) & 31u;
-      const uint64_t rem = jb.total_bits - 64 * T;
-      E = rem < 64 ? (uint32_t)rem : 64u;
+    if (active) {
+      const uint64_t chunks_left = jb.n_threads - tile * kTPB;  // > 0 for an active tile
+      if (lane < chunks_left) {
+        gap = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * lane) & 31)) & 31u;
+        const uint64_t bits_left = jb.total_bits - tile * (64 * kTPB);
+        if (bits_left >= 64 * (uint64_t)kTPB) {
+          E = 64;
+        } else {
+          const uint32_t r = (uint32_t)bits_left - 64 * lane;
+          E = r < 64 ? r : 64u;
+        }
+      }
     }
 
     // clear the staging bytes this tile uses (plus the spill word)
-    const uint32_t span = (uint32_t)(hi - a);
-    const uint32_t zero_bytes = (span + 8 + 15) & ~15u;
-    for (uint32_t i = tid * 16; i < zero_bytes; i += kTPB * 16)
-      *(uint4 *)(out_lds + i) = make_uint4(0, 0, 0, 0);
+    if (active) {
+      const uint32_t zero_bytes = (hi_r + 8 + 15) & ~15u;
+      for (uint32_t i = lane * 16; i < zero_bytes; i += kTPB * 16)
+        *(uint4 *)(out_lds + i) = make_uint4(0, 0, 0, 0);
+    }
 
     // phase 1: count the codes that start in [gap, E)
     uint32_t cnt = 0;
     {
       uint32_t p = gap;
-      while (p + kK < E) {
-        const uint32_t win = window(w0, w1, w2, p);
-        const uint32_t h = dtab_words[2 * (win & (kDtabEntries - 1)) + 1];
-        uint32_t adv = (h >> 24) & 15;
-        uint32_t nc = h >> 28;
-        if (adv == 0) {
-          adv = long_code<CHECKED>(lut_lds, n_luts, win, batch.err) >> 8;
-          nc = 1;
-        }
-        cnt += nc;
-        p += adv;
-      }
-      while (p < E) {
-        const uint32_t win = window(w0, w1, w2, p);
-        const uint32_t h = dtab_words[2 * (win & (kDtabEntries - 1)) + 1];
-        uint32_t adv = (h >> 24) & 15;
-        uint32_t starts = (h >> 8) & 0xFFFu;
-        if (adv == 0) {
-          adv = long_code<CHECKED>(lut_lds, n_luts, win, batch.err) >> 8;
-          starts = 1;
-        }
-        cnt += __popc(starts & ((1u << (E - p)) - 1));  // E - p <= 12 here
-        p += adv;
-      }
+      while (p < 32 && p + kK < E)
+        p += count_step<CHECKED>(dtw, lut_lds, n_luts, funnel(cur.w1, cur.w0, p), batch.err, cnt);
+      while (p + kK < E)
+        p += count_step<CHECKED>(dtw, lut_lds, n_luts, funnel(cur.w2, cur.w1, p), batch.err, cnt);
+      while (p < E)
+        p += count_step_clip<CHECKED>(dtw, lut_lds, n_luts, window(cur.w0, cur.w1, cur.w2, p), E - p,
+                                      batch.err, cnt);
     }
 
-    uint32_t total;
-    const uint32_t off = block_exclusive_sum(cnt, wsum, &total);
-    if (CHECKED && tid == 0 && (uint64_t)total != hi - lo) atomicOr(batch.err, DF_DEVERR_COUNT);
+    // prefix sum of the counts over the tile's 256 lanes
+    const uint32_t wid = tid >> 6;
+    const uint32_t x = wave_inclusive_sum(cnt);
+    if ((tid & 63) == 63) wsum[wid] = x;
+    __syncthreads();
+    const uint32_t *ws = wsum + 4 * grp;
+    const uint32_t s0 = ws[0], s1 = ws[1], s2 = ws[2], s3 = ws[3];
+    const uint32_t wq = wid & 3;
+    const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
+    if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
+      atomicOr(batch.err, DF_DEVERR_COUNT);
 
     // phase 2: decode again, OR the symbol bytes into the staging buffer
     {
       uint32_t p = gap;
-      uint32_t q = (uint32_t)(lo - a) + off;
-      while (p + kK < E) {
-        const uint32_t win = window(w0, w1, w2, p);
-        const uint2 e = *(const uint2 *)(dtab_lds + (win & (kDtabEntries - 1)));
-        uint32_t adv = (e.y >> 24) & 15;
-        uint32_t nc = e.y >> 28;
-        uint32_t s0 = e.x, s1 = e.y & 0xFFu;
-        if (adv == 0) {
-          const uint32_t r = long_code<CHECKED>(lut_lds, n_luts, win, batch.err);
-          adv = r >> 8;
-          s0 = KIND == DF_KIND_BF16 ? rot_right1(r & 0xFFu) : (r & 0xFFu);
-          s1 = 0;
-          nc = 1;
-        }
-        put_bytes(out_lds, q, qmax, s0, s1);
-        q += nc;
-        p += adv;
-      }
-      while (p < E) {
-        const uint32_t win = window(w0, w1, w2, p);
-        const uint2 e = *(const uint2 *)(dtab_lds + (win & (kDtabEntries - 1)));
-        uint32_t adv = (e.y >> 24) & 15;
-        uint32_t starts = (e.y >> 8) & 0xFFFu;
-        uint32_t s0 = e.x, s1 = e.y & 0xFFu;
-        if (adv == 0) {
-          const uint32_t r = long_code<CHECKED>(lut_lds, n_luts, win, batch.err);
-          adv = r >> 8;
-          s0 = KIND == DF_KIND_BF16 ? rot_right1(r & 0xFFu) : (r & 0xFFu);
-          s1 = 0;
-          starts = 1;
-        }
-        const uint32_t nc = __popc(starts & ((1u << (E - p)) - 1));
-        if (nc < 5) {
-          s1 = 0;
-          if (nc < 4) s0 &= (1u << (8 * nc)) - 1;
-        }
-        put_bytes(out_lds, q, qmax, s0, s1);
-        q += nc;
-        p += adv;
-      }
+      uint32_t q = lo_r + off;
+      while (p < 32 && p + kK < E)
+        p += decode_step<KIND, CHECKED, false>(dtab_lds, lut_lds, n_luts, funnel(cur.w1, cur.w0, p), 0,
+                                               batch.err, out_lds, q, qmax);
+      while (p + kK < E)
+        p += decode_step<KIND, CHECKED, false>(dtab_lds, lut_lds, n_luts, funnel(cur.w2, cur.w1, p), 0,
+                                               batch.err, out_lds, q, qmax);
+      while (p < E)
+        p += decode_step<KIND, CHECKED, true>(dtab_lds, lut_lds, n_luts, window(cur.w0, cur.w1, cur.w2, p),
+                                              E - p, batch.err, out_lds, q, qmax);
     }
     __syncthreads();
 
     // one coalesced pass: aligned 16-byte stores of the tile's output range
     if (KIND == DF_KIND_BF16) {
-      uint16_t *dst = (uint16_t *)jb.dst;
-      const uint32_t groups = (uint32_t)(((hi + 7) >> 3) - (lo >> 3));
-      for (uint32_t g = tid; g < groups; g += kTPB) {
-        const uint64_t e0 = a + 8ull * g;
-        const uint2 ex = *(const uint2 *)(out_lds + 8 * g);
-        const uint2 sv = *(const uint2 *)(jb.sm + e0);
-        const uint2 o01 = merge4(ex.x, sv.x);
-        const uint2 o23 = merge4(ex.y, sv.y);
-        if (e0 >= lo && e0 + 8 <= hi) {
-          *(uint4 *)(dst + e0) = make_uint4(o01.x, o01.y, o23.x, o23.y);
-        } else {
-          const uint32_t o[4] = {o01.x, o01.y, o23.x, o23.y};
-          for (uint32_t k = 0; k < 8; k++)
-            if (e0 + k >= lo && e0 + k < hi) dst[e0 + k] = (uint16_t)(o[k >> 1] >> (16 * (k & 1)));
+      uint16_t *dst_t = (uint16_t *)jb.dst + a;
+#pragma unroll
+      for (uint32_t k = 0; k < kPrefetch; k++) {
+        const uint32_t g = lane + k * kTPB;
+        if (g < ngroups) {
+          const uint32_t e0 = 8 * g;
+          const uint2 ex = *(const uint2 *)(out_lds + e0);
+          const uint2 o01 = merge4(ex.x, smv[k].x);
+          const uint2 o23 = merge4(ex.y, smv[k].y);
+          const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
+          if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
+          else store_partial(dst_t, e0, lo_r, hi_r, o);
         }
       }
+      for (uint32_t g = lane + kPrefetch * kTPB; g < ngroups; g += kTPB) {
+        const uint32_t e0 = 8 * g;
+        const uint2 ex = *(const uint2 *)(out_lds + e0);
+        const uint2 sv = *(const uint2 *)(sm_t + e0);
+        const uint2 o01 = merge4(ex.x, sv.x);
+        const uint2 o23 = merge4(ex.y, sv.y);
+        const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
+        if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
+        else store_partial(dst_t, e0, lo_r, hi_r, o);
+      }
     } else {
-      uint8_t *dst = (uint8_t *)jb.dst;
-      const uint32_t groups = (uint32_t)(((hi + 15) >> 4) - (lo >> 4));
-      for (uint32_t g = tid; g < groups; g += kTPB) {
-        const uint64_t e0 = a + 16ull * g;
-        const uint4 v = *(const uint4 *)(out_lds + 16 * g);
-        if (e0 >= lo && e0 + 16 <= hi) {
-          *(uint4 *)(dst + e0) = v;
-        } else {
-          const uint32_t o[4] = {v.x, v.y, v.z, v.w};
-          for (uint32_t k = 0; k < 16; k++)
-            if (e0 + k >= lo && e0 + k < hi) dst[e0 + k] = (uint8_t)(o[k >> 2] >> (8 * (k & 3)));
-        }
+      uint8_t *dst_t = (uint8_t *)jb.dst + a;
+      for (uint32_t g = lane; g < ngroups; g += kTPB) {
+        const uint32_t e0 = 16 * g;
+        const uint4 v = *(const uint4 *)(out_lds + e0);
+        if (e0 >= lo_r && e0 + 16 <= hi_r) *(uint4 *)(dst_t + e0) = v;
+        else store_partial(dst_t, e0, lo_r, hi_r, v);
       }
     }
     __syncthreads();
@@ -375,7 +481,7 @@ df_status check_view(const df_device_view *v, const void *dst) {
   return DF_OK;
 }
 
-uint32_t lds_out_bytes_for(uint32_t max_tile_elems) {
+uint32_t out_bytes_for(uint32_t max_tile_elems) {
   // tile range rounded down to a 16-element granule, plus the 8-byte spill
   // of the last OR, rounded to 16, plus one spare granule
   return ((max_tile_elems + 15 + 8 + 15) & ~15u) + 16;
@@ -413,21 +519,37 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
       if (v.n_luts > max_luts) max_luts = v.n_luts;
     }
     if (nj == 0) continue;
-    const uint32_t out_bytes = lds_out_bytes_for(max_elems);
-    const size_t lds = (size_t)out_bytes + kDtabBytes + (size_t)max_luts * 512;
-    if (lds > (size_t)props.max_lds) return DF_ERR_ARG;
+    const uint32_t out_bytes = out_bytes_for(max_elems);
+    const uint32_t lut_bytes = max_luts * 512;
+    // tile groups per workgroup: the choice that keeps the most waves
+    // resident per CU (LDS is the limit: the tables are shared per workgroup)
+    uint32_t groups = 0;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, (int)kTPB, lds) != hipSuccess)
-      return DF_ERR_HIP;
-    if (per_cu < 1) per_cu = 1;
+    size_t lds = 0;
+    for (uint32_t g = kMaxGroups; g >= 1; g /= 2) {
+      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes;
+      if (need > (size_t)props.max_lds) continue;
+      int occ = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
+          hipSuccess)
+        return DF_ERR_HIP;
+      if (occ < 1) continue;
+      if (groups == 0 || (uint64_t)occ * g > (uint64_t)per_cu * groups) {
+        groups = g;
+        per_cu = occ;
+        lds = need;
+      }
+    }
+    if (groups == 0) return DF_ERR_ARG;
     uint64_t budget = (uint64_t)props.cus * (uint64_t)per_cu;
     if (budget < nj) budget = nj;
     uint32_t wg = 0;
     for (uint32_t k = 0; k < nj; k++) {
       const df_device_view &v = views[idx[k]];
       uint64_t share = budget * v.n_tiles / tiles;
+      const uint64_t need = (v.n_tiles + groups - 1) / groups;
       if (share < 1) share = 1;
-      if (share > v.n_tiles) share = v.n_tiles;
+      if (share > need) share = need;
       Job &jb = b.job[k];
       jb.bits = (const uint32_t *)v.bitstream;
       jb.gaps = (const uint32_t *)v.gaps;
@@ -447,9 +569,10 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
       wg += (uint32_t)share;
     }
     b.count = nj;
-    b.lds_out_bytes = out_bytes;
+    b.lut_bytes = lut_bytes;
+    b.out_bytes = out_bytes;
     b.err = err;
-    hipLaunchKernelGGL(fn, dim3(wg), dim3(kTPB), lds, stream, b);
+    hipLaunchKernelGGL(fn, dim3(wg), dim3(groups * kTPB), lds, stream, b);
     if (hipGetLastError() != hipSuccess) return DF_ERR_HIP;
   }
   return DF_OK;
