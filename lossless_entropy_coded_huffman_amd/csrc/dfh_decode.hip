@@ -81,17 +81,27 @@ __device__ __forceinline__ uint32_t window(uint32_t w0, uint32_t w1, uint32_t w2
   return (uint32_t)((((uint64_t)hi << 32) | lo) >> (p & 31));
 }
 
-// Bits [s, s + 32) of hi:lo, s taken mod 32 (v_alignbit_b32).
-__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t s) {
-  return (uint32_t)((((uint64_t)hi << 32) | lo) >> (s & 31));
+// LDS is addressed through address-space-3 pointers made from byte offsets:
+// the kernel declares no static LDS, so its dynamic LDS starts at offset 0
+// and table offsets fold into the ds instructions' immediate fields.
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) v2u lds_v2;
+typedef __attribute__((address_space(3))) v4u lds_v4;
+template <class T>
+__device__ __forceinline__ T *lds(uint32_t byte_offset) {
+  return (T *)(uintptr_t)byte_offset;
 }
 
-// One code through the hierarchical tables: returns (length << 8) | symbol.
-// A prefix with no code (possible only for an incomplete code or a corrupt
-// stream) reports DF_DEVERR_CODE in checked launches and consumes one bit.
+// One code through the hierarchical tables (at LDS offset kDtabBytes):
+// returns (length << 8) | symbol.  A prefix with no code (possible only for
+// an incomplete code or a corrupt stream) reports DF_DEVERR_CODE in checked
+// launches and consumes one bit.
 template <bool CHECKED>
-__device__ __forceinline__ uint32_t long_code(const uint16_t *lut, uint32_t n_luts, uint32_t win,
-                                              uint32_t *err) {
+__device__ __forceinline__ uint32_t long_code(uint32_t n_luts, uint32_t win, uint32_t *err) {
+  const lds_u16 *lut = lds<const lds_u16>(kDtabBytes);
   uint32_t e = lut[win & 255];
   uint32_t sh = 8;
   for (int d = 0; d < 3 && (e & 0x8000u); d++) {
@@ -122,17 +132,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
   return x;
 }
 
-// OR up to five symbol bytes (s0 = bytes 0..3, s1 = byte 4) into the staging
-// buffer at byte q; they span at most two aligned words.
-__device__ __forceinline__ void put_bytes(uint8_t *out, uint32_t q, uint32_t qmax, uint32_t s0,
-                                          uint32_t s1) {
-  const uint32_t qq = q < qmax ? q : qmax;
-  const uint64_t v = ((((uint64_t)s1) << 32) | s0) << ((qq & 3) * 8);
-  uint32_t *w = (uint32_t *)(out + (qq & ~3u));
-  atomicOr(w, (uint32_t)v);
-  atomicOr(w + 1, (uint32_t)(v >> 32));
-}
-
 // Merge four exponent bytes (rotated right by one bit) with four
 // sign|mantissa bytes into four BF16 values (two words):
 // BF16 low byte = e0 << 7 | mantissa, high byte = sign << 7 | e >> 1.
@@ -144,65 +143,51 @@ __device__ __forceinline__ uint2 merge4(uint32_t e4, uint32_t s4) {
   return make_uint2((x0 & 0x7F7F7F7Fu) | (y0 & 0x80808080u), (x1 & 0x7F7F7F7Fu) | (y1 & 0x80808080u));
 }
 
-// Phase-1 lookup: counts the codes of one table entry, returns bits used.
+// Phase-1 lookup at chunk bit p: adds the number of the entry's codes that
+// start before the chunk end E (bits [8, 8 + min(E - p, 12)) of the entry's
+// high word are its start mask) and returns the bits the entry consumes.
 template <bool CHECKED>
-__device__ __forceinline__ uint32_t count_step(const uint32_t *dtw, const uint16_t *lut, uint32_t n_luts,
-                                               uint32_t win, uint32_t *err, uint32_t &cnt) {
-  const uint32_t h = dtw[((win & (kDtabEntries - 1)) << 1) | 1];
+__device__ __forceinline__ uint32_t count_step(uint32_t n_luts, uint32_t win, uint32_t rem, uint32_t *err,
+                                               uint32_t &cnt) {
+  uint32_t h = lds<const lds_u32>(4)[(win & (kDtabEntries - 1)) << 1];
   uint32_t adv = (h >> 24) & 15;
-  uint32_t nc = h >> 28;
   if (adv == 0) {
-    adv = long_code<CHECKED>(lut, n_luts, win, err) >> 8;
-    nc = 1;
+    adv = long_code<CHECKED>(n_luts, win, err) >> 8;
+    h = 1u << 8;
   }
-  cnt += nc;
+  cnt += __popc(__builtin_amdgcn_ubfe(h, 8, rem < kK ? rem : kK));
   return adv;
 }
 
-// Phase-1 lookup near the chunk end: only codes starting before bit r of the
-// window count (1 <= r <= 12).
-template <bool CHECKED>
-__device__ __forceinline__ uint32_t count_step_clip(const uint32_t *dtw, const uint16_t *lut,
-                                                    uint32_t n_luts, uint32_t win, uint32_t r,
-                                                    uint32_t *err, uint32_t &cnt) {
-  const uint32_t h = dtw[((win & (kDtabEntries - 1)) << 1) | 1];
-  uint32_t adv = (h >> 24) & 15;
-  uint32_t starts = (h >> 8) & 0xFFFu;
-  if (adv == 0) {
-    adv = long_code<CHECKED>(lut, n_luts, win, err) >> 8;
-    starts = 1;
-  }
-  cnt += __popc(starts & ((1u << r) - 1));
-  return adv;
-}
-
-// Phase-2 lookup: writes the entry's symbol bytes at q, returns bits used.
-// CLIP: keep only codes starting before bit r of the window.
-template <int KIND, bool CHECKED, bool CLIP>
-__device__ __forceinline__ uint32_t decode_step(const uint64_t *dtab, const uint16_t *lut,
-                                                uint32_t n_luts, uint32_t win, uint32_t r, uint32_t *err,
-                                                uint8_t *out, uint32_t &q, uint32_t qmax) {
-  const uint2 e = *(const uint2 *)(dtab + (win & (kDtabEntries - 1)));
+// Phase-2 lookup at chunk bit p (rem = E - p): ORs the symbol bytes of the
+// entry's codes that start before E into the staging buffer at LDS byte q
+// and advances q; returns the bits the entry consumes.
+template <int KIND, bool CHECKED>
+__device__ __forceinline__ uint32_t decode_step(uint32_t n_luts, uint32_t win, uint32_t rem, uint32_t *err,
+                                                uint32_t &q) {
+  const v2u e = lds<const lds_v2>(0)[win & (kDtabEntries - 1)];
   uint32_t adv = (e.y >> 24) & 15;
   uint32_t nc = e.y >> 28;
   uint32_t s0 = e.x, s1 = e.y & 0xFFu;
-  uint32_t starts = (e.y >> 8) & 0xFFFu;
-  if (adv == 0) {
-    const uint32_t c = long_code<CHECKED>(lut, n_luts, win, err);
-    adv = c >> 8;
-    s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
-    s1 = 0;
-    nc = 1;
-    starts = 1;
-  }
-  if (CLIP) {
-    nc = __popc(starts & ((1u << r) - 1));
+  if (adv == 0 || rem < adv) {  // rare: a long code, or the entry runs past the chunk end
+    uint32_t starts = (e.y >> 8) & 0xFFFu;
+    if (adv == 0) {
+      const uint32_t c = long_code<CHECKED>(n_luts, win, err);
+      adv = c >> 8;
+      s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+      s1 = 0;
+      starts = 1;
+    }
+    nc = __popc(starts & ((1u << (rem < kK ? rem : kK)) - 1));
     if (nc < 5) {
       s1 = 0;
       if (nc < 4) s0 &= (1u << (8 * nc)) - 1;
     }
   }
-  put_bytes(out, q, qmax, s0, s1);
+  const uint64_t v = ((((uint64_t)s1) << 32) | s0) << ((q & 3) * 8);
+  lds_u32 *w = lds<lds_u32>(q & ~3u);
+  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   q += nc;
   return adv;
 }
@@ -249,9 +234,8 @@ __device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, ui
 template <int KIND, bool CHECKED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ uint32_t wsum[4 * kMaxGroups];
-
+  // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
+  // one staging buffer per tile group, then the per-wave scan sums
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
@@ -261,19 +245,15 @@ void decode_kernel(const Batch batch) {
   const uint32_t grp = __builtin_amdgcn_readfirstlane(tid / kTPB);
   const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
-
-  uint64_t *dtab_lds = (uint64_t *)smem;
-  const uint32_t *dtw = (const uint32_t *)smem;
-  uint16_t *lut_lds = (uint16_t *)(smem + kDtabBytes);
-  uint8_t *out_lds = smem + kDtabBytes + batch.lut_bytes + grp * batch.out_bytes;
-  const uint32_t qmax = batch.out_bytes - 8;
+  const uint32_t out_base = kDtabBytes + batch.lut_bytes + grp * batch.out_bytes;  // LDS byte offset
+  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * batch.out_bytes);
 
   {  // stage the tables once per workgroup
-    const uint4 *src = (const uint4 *)jb.dtab;
-    uint4 *dl = (uint4 *)dtab_lds;
+    const v4u *src = (const v4u *)jb.dtab;
+    lds_v4 *dl = lds<lds_v4>(0);
     for (uint32_t i = tid; i < kDtabBytes / 16; i += blockDim.x) dl[i] = src[i];
-    const uint4 *ls = (const uint4 *)jb.lut;
-    uint4 *ll = (uint4 *)lut_lds;
+    const v4u *ls = (const v4u *)jb.lut;
+    lds_v4 *ll = lds<lds_v4>(kDtabBytes);
     for (uint32_t i = tid; i < n_luts * 32; i += blockDim.x) ll[i] = ls[i];
   }
 
@@ -337,60 +317,52 @@ void decode_kernel(const Batch batch) {
     // clear the staging bytes this tile uses (plus the spill word)
     if (active) {
       const uint32_t zero_bytes = (hi_r + 8 + 15) & ~15u;
-      for (uint32_t i = lane * 16; i < zero_bytes; i += kTPB * 16)
-        *(uint4 *)(out_lds + i) = make_uint4(0, 0, 0, 0);
+      lds_v4 *z = lds<lds_v4>(out_base);
+      for (uint32_t i = lane; i < zero_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
     }
 
     // phase 1: count the codes that start in [gap, E)
     uint32_t cnt = 0;
-    {
-      uint32_t p = gap;
-      while (p < 32 && p + kK < E)
-        p += count_step<CHECKED>(dtw, lut_lds, n_luts, funnel(cur.w1, cur.w0, p), batch.err, cnt);
-      while (p + kK < E)
-        p += count_step<CHECKED>(dtw, lut_lds, n_luts, funnel(cur.w2, cur.w1, p), batch.err, cnt);
-      while (p < E)
-        p += count_step_clip<CHECKED>(dtw, lut_lds, n_luts, window(cur.w0, cur.w1, cur.w2, p), E - p,
-                                      batch.err, cnt);
-    }
+    for (uint32_t p = gap; p < E;)
+      p += count_step<CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), E - p, batch.err, cnt);
 
     // prefix sum of the counts over the tile's 256 lanes
     const uint32_t wid = tid >> 6;
     const uint32_t x = wave_inclusive_sum(cnt);
     if ((tid & 63) == 63) wsum[wid] = x;
     __syncthreads();
-    const uint32_t *ws = wsum + 4 * grp;
+    const lds_u32 *ws = wsum + 4 * grp;
     const uint32_t s0 = ws[0], s1 = ws[1], s2 = ws[2], s3 = ws[3];
     const uint32_t wq = wid & 3;
     const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
 
-    // phase 2: decode again, OR the symbol bytes into the staging buffer
+    // phase 2: decode again, OR the symbol bytes into the staging buffer.
+    // A lane whose codes would not fit the buffer (only with corrupt offsets
+    // or stream) skips the phase, so LDS writes stay inside the buffer.
     {
-      uint32_t p = gap;
-      uint32_t q = lo_r + off;
-      while (p < 32 && p + kK < E)
-        p += decode_step<KIND, CHECKED, false>(dtab_lds, lut_lds, n_luts, funnel(cur.w1, cur.w0, p), 0,
-                                               batch.err, out_lds, q, qmax);
-      while (p + kK < E)
-        p += decode_step<KIND, CHECKED, false>(dtab_lds, lut_lds, n_luts, funnel(cur.w2, cur.w1, p), 0,
-                                               batch.err, out_lds, q, qmax);
-      while (p < E)
-        p += decode_step<KIND, CHECKED, true>(dtab_lds, lut_lds, n_luts, window(cur.w0, cur.w1, cur.w2, p),
-                                              E - p, batch.err, out_lds, q, qmax);
+      uint32_t q = out_base + lo_r + off;
+      uint32_t end = E;
+      if (lo_r + off + cnt + 8 > batch.out_bytes) {
+        end = 0;
+        if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
+      }
+      for (uint32_t p = gap; p < end;)
+        p += decode_step<KIND, CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), end - p, batch.err, q);
     }
     __syncthreads();
 
     // one coalesced pass: aligned 16-byte stores of the tile's output range
     if (KIND == DF_KIND_BF16) {
       uint16_t *dst_t = (uint16_t *)jb.dst + a;
+      const lds_v2 *ex_t = lds<const lds_v2>(out_base);
 #pragma unroll
       for (uint32_t k = 0; k < kPrefetch; k++) {
         const uint32_t g = lane + k * kTPB;
         if (g < ngroups) {
           const uint32_t e0 = 8 * g;
-          const uint2 ex = *(const uint2 *)(out_lds + e0);
+          const v2u ex = ex_t[g];
           const uint2 o01 = merge4(ex.x, smv[k].x);
           const uint2 o23 = merge4(ex.y, smv[k].y);
           const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
@@ -400,7 +372,7 @@ void decode_kernel(const Batch batch) {
       }
       for (uint32_t g = lane + kPrefetch * kTPB; g < ngroups; g += kTPB) {
         const uint32_t e0 = 8 * g;
-        const uint2 ex = *(const uint2 *)(out_lds + e0);
+        const v2u ex = ex_t[g];
         const uint2 sv = *(const uint2 *)(sm_t + e0);
         const uint2 o01 = merge4(ex.x, sv.x);
         const uint2 o23 = merge4(ex.y, sv.y);
@@ -410,11 +382,12 @@ void decode_kernel(const Batch batch) {
       }
     } else {
       uint8_t *dst_t = (uint8_t *)jb.dst + a;
+      const lds_v4 *ex_t = lds<const lds_v4>(out_base);
       for (uint32_t g = lane; g < ngroups; g += kTPB) {
         const uint32_t e0 = 16 * g;
-        const uint4 v = *(const uint4 *)(out_lds + e0);
-        if (e0 >= lo_r && e0 + 16 <= hi_r) *(uint4 *)(dst_t + e0) = v;
-        else store_partial(dst_t, e0, lo_r, hi_r, v);
+        const v4u v = ex_t[g];
+        if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
+        else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
       }
     }
     __syncthreads();
@@ -527,7 +500,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     int per_cu = 0;
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g /= 2) {
-      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes;
+      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes + 16 * g;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
