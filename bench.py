@@ -116,8 +116,8 @@ def cpu_baseline(containers, srcs, kind):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3, help="device copies of the compressed input")
     ap.add_argument("--workload", default="llama3_8b_block_bf16",

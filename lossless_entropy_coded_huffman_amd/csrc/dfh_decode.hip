@@ -51,6 +51,9 @@ constexpr uint32_t kK = DF_DTAB_BITS;           // multi-code table index width
 constexpr uint32_t kDtabEntries = 1u << kK;
 constexpr uint32_t kDtabBytes = kDtabEntries * 8;
 constexpr uint32_t kPrefetch = 4;  // sign|mantissa 8-byte groups requested ahead per lane
+// staging bytes past a tile's last element that phase 2 may touch: up to four
+// lookahead symbol bytes, widened to the two words of one OR
+constexpr uint32_t kSlack = 12;
 
 struct Job {
   const uint32_t *bits;  // bitstream, little-endian 32-bit words
@@ -159,30 +162,25 @@ __device__ __forceinline__ uint32_t count_step(uint32_t n_luts, uint32_t win, ui
   return adv;
 }
 
-// Phase-2 lookup at chunk bit p (rem = E - p): ORs the symbol bytes of the
-// entry's codes that start before E into the staging buffer at LDS byte q
-// and advances q; returns the bits the entry consumes.
+// Phase-2 lookup: ORs the symbol bytes of the entry's codes into the staging
+// buffer at LDS byte q, advances q and returns the bits the entry consumes.
+// No clipping at the chunk end: codes of a lane's last lookup that start
+// past its chunk are the next lane's first codes (code boundaries are a
+// property of the stream), written to the same positions with the same
+// values by that lane, so the OR is idempotent; past the tile's last code
+// they land in the staging slack, which is never stored.
 template <int KIND, bool CHECKED>
-__device__ __forceinline__ uint32_t decode_step(uint32_t n_luts, uint32_t win, uint32_t rem, uint32_t *err,
-                                                uint32_t &q) {
+__device__ __forceinline__ uint32_t decode_step(uint32_t n_luts, uint32_t win, uint32_t *err, uint32_t &q) {
   const v2u e = lds<const lds_v2>(0)[win & (kDtabEntries - 1)];
   uint32_t adv = (e.y >> 24) & 15;
   uint32_t nc = e.y >> 28;
   uint32_t s0 = e.x, s1 = e.y & 0xFFu;
-  if (adv == 0 || rem < adv) {  // rare: a long code, or the entry runs past the chunk end
-    uint32_t starts = (e.y >> 8) & 0xFFFu;
-    if (adv == 0) {
-      const uint32_t c = long_code<CHECKED>(n_luts, win, err);
-      adv = c >> 8;
-      s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
-      s1 = 0;
-      starts = 1;
-    }
-    nc = __popc(starts & ((1u << (rem < kK ? rem : kK)) - 1));
-    if (nc < 5) {
-      s1 = 0;
-      if (nc < 4) s0 &= (1u << (8 * nc)) - 1;
-    }
+  if (adv == 0) {  // rare: a code longer than the table's index width
+    const uint32_t c = long_code<CHECKED>(n_luts, win, err);
+    adv = c >> 8;
+    s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+    s1 = 0;
+    nc = 1;
   }
   const uint64_t v = ((((uint64_t)s1) << 32) | s0) << ((q & 3) * 8);
   lds_u32 *w = lds<lds_u32>(q & ~3u);
@@ -248,36 +246,51 @@ void decode_kernel(const Batch batch) {
   const uint32_t out_base = kDtabBytes + batch.lut_bytes + grp * batch.out_bytes;  // LDS byte offset
   lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * batch.out_bytes);
 
-  {  // stage the tables once per workgroup
-    const v4u *src = (const v4u *)jb.dtab;
+  {  // stage the tables once per workgroup: the first four 16-byte words per
+     // lane (all a 1024-lane workgroup needs for up to 64 levels) with every
+     // load issued before any write, the rest one by one
+    const uint32_t total = kDtabBytes / 16 + n_luts * 32;  // 16-byte words: table, then levels
+    const v4u *dsrc = (const v4u *)jb.dtab;
+    const v4u *lsrc = (const v4u *)jb.lut - kDtabBytes / 16;
     lds_v4 *dl = lds<lds_v4>(0);
-    for (uint32_t i = tid; i < kDtabBytes / 16; i += blockDim.x) dl[i] = src[i];
-    const v4u *ls = (const v4u *)jb.lut;
-    lds_v4 *ll = lds<lds_v4>(kDtabBytes);
-    for (uint32_t i = tid; i < n_luts * 32; i += blockDim.x) ll[i] = ls[i];
+    const uint32_t i0 = tid, i1 = tid + blockDim.x, i2 = tid + 2 * blockDim.x, i3 = tid + 3 * blockDim.x;
+    const v4u z = {0u, 0u, 0u, 0u};
+    const v4u t0 = i0 < total ? (i0 < kDtabBytes / 16 ? dsrc[i0] : lsrc[i0]) : z;
+    const v4u t1 = i1 < total ? (i1 < kDtabBytes / 16 ? dsrc[i1] : lsrc[i1]) : z;
+    const v4u t2 = i2 < total ? (i2 < kDtabBytes / 16 ? dsrc[i2] : lsrc[i2]) : z;
+    const v4u t3 = i3 < total ? (i3 < kDtabBytes / 16 ? dsrc[i3] : lsrc[i3]) : z;
+    if (i0 < total) dl[i0] = t0;
+    if (i1 < total) dl[i1] = t1;
+    if (i2 < total) dl[i2] = t2;
+    if (i3 < total) dl[i3] = t3;
+    for (uint32_t i = tid + 4 * blockDim.x; i < total; i += blockDim.x)
+      dl[i] = i < kDtabBytes / 16 ? dsrc[i] : lsrc[i];
   }
 
   const uint64_t step = (uint64_t)jb.wg_count * groups;
   uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
   ChunkRegs nxt = load_chunk(jb, base + grp, lane);
-  uint64_t nlo = 0, nhi = 0;
-  if (base + grp < jb.n_tiles) {
-    nlo = jb.tile_out[base + grp];
-    nhi = jb.tile_out[base + grp + 1];
-  }
+  // a tile's first and last output index: lane 0 of each wave loads
+  // tile_out[t], lane 1 tile_out[t + 1]; kept in vector registers until the
+  // step that uses them
+  uint64_t nto = 0;
+  if (base + grp < jb.n_tiles) nto = jb.tile_out[base + grp + (lane & 1)];
   __syncthreads();
 
   for (; base < jb.n_tiles; base += step) {
     const uint64_t tile = base + grp;  // wave-uniform
     const bool active = tile < jb.n_tiles;
     const ChunkRegs cur = nxt;
-    uint64_t lo = nlo, hi = nhi;
-    // next step's stream words, gaps and offsets go in flight now
+    uint64_t lo = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 0) << 32) |
+                  __builtin_amdgcn_readlane((uint32_t)nto, 0);
+    uint64_t hi = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 1) << 32) |
+                  __builtin_amdgcn_readlane((uint32_t)nto, 1);
+    // take this step's stream words now, while nothing newer is in flight
+    // (the memory counter retires in order), then put the next step's
+    // words and offsets in flight
+    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
     nxt = load_chunk(jb, tile + step, lane);
-    if (tile + step < jb.n_tiles) {
-      nlo = jb.tile_out[tile + step];
-      nhi = jb.tile_out[tile + step + 1];
-    }
+    if (tile + step < jb.n_tiles) nto = jb.tile_out[tile + step + (lane & 1)];
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
     if (hi - lo > jb.max_tile_elems) hi = lo + jb.max_tile_elems;
@@ -314,9 +327,10 @@ void decode_kernel(const Batch batch) {
       }
     }
 
-    // clear the staging bytes this tile uses (plus the spill word)
+    // clear the staging bytes this tile uses, plus the slack written by the
+    // last lane's lookahead codes
     if (active) {
-      const uint32_t zero_bytes = (hi_r + 8 + 15) & ~15u;
+      const uint32_t zero_bytes = (hi_r + kSlack + 15) & ~15u;
       lds_v4 *z = lds<lds_v4>(out_base);
       for (uint32_t i = lane; i < zero_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
     }
@@ -344,12 +358,12 @@ void decode_kernel(const Batch batch) {
     {
       uint32_t q = out_base + lo_r + off;
       uint32_t end = E;
-      if (lo_r + off + cnt + 8 > batch.out_bytes) {
+      if (lo_r + off + cnt + kSlack > batch.out_bytes) {
         end = 0;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
       }
       for (uint32_t p = gap; p < end;)
-        p += decode_step<KIND, CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), end - p, batch.err, q);
+        p += decode_step<KIND, CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), batch.err, q);
     }
     __syncthreads();
 
@@ -455,9 +469,9 @@ df_status check_view(const df_device_view *v, const void *dst) {
 }
 
 uint32_t out_bytes_for(uint32_t max_tile_elems) {
-  // tile range rounded down to a 16-element granule, plus the 8-byte spill
-  // of the last OR, rounded to 16, plus one spare granule
-  return ((max_tile_elems + 15 + 8 + 15) & ~15u) + 16;
+  // tile range rounded down to a 16-element granule, plus the slack of the
+  // last lane's lookahead writes, rounded to 16, plus one spare granule
+  return ((max_tile_elems + 15 + kSlack + 15) & ~15u) + 16;
 }
 
 df_status launch(const df_device_view *views, void *const *dsts, uint32_t count, uint32_t *err,
