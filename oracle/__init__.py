@@ -85,6 +85,7 @@ def _load():
             "oracle_decode_serial": (I, [I, P, P, U64, U64, P, P]),
             "oracle_decode_tiles": (I, [I, P, P, U64, P, P, U64, U64, P, P, I]),
             "oracle_check_dtab": (ctypes.c_int64, [I, P, P, I]),
+            "oracle_decode_tile_range": (I, [I, P, P, U64, P, P, U64, U64, U64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -235,6 +236,30 @@ def decode_tiles(c: dict, cpu_threads: int = 1, out: np.ndarray | None = None) -
     rc = _load().oracle_decode_tiles(kind, _ptr(ln), _ptr(bs), bs.size, _ptr(gaps), _ptr(to),
                                      int(c["n_tiles"]), int(c["n_threads"]), _ptr(sm), _ptr(out),
                                      int(cpu_threads))
+    if rc != 0:
+        raise ValueError("undecodable stream")
+    return out
+
+
+def decode_tile_range(c: dict, b0: int, b1: int) -> np.ndarray:
+    """Decode tiles [b0, b1) of a container (one CPU thread); returns the
+    elements tile_out[b0] .. tile_out[b1] - 1.  For sampled checks of
+    containers too large to decode whole."""
+    kind = int(c["kind"])
+    to = np.ascontiguousarray(c["tile_out"], np.uint64)
+    lo, hi = int(to[b0]), int(to[b1])
+    out = np.empty(hi - lo, np.uint16 if kind == KIND_BF16 else np.uint8)
+    ln = np.ascontiguousarray(c["lengths"], np.uint8)
+    bs = np.ascontiguousarray(c["bitstream"], np.uint8)
+    gaps = np.ascontiguousarray(c["gaps"], np.uint8)
+    sm = None if kind == KIND_U8 else np.ascontiguousarray(c["sign_mantissa"], np.uint8)
+    # dst points lo elements before the buffer so that element i lands at i - lo;
+    # the worker writes only indices in [lo, hi)
+    esz = out.itemsize
+    base = out.ctypes.data - lo * esz
+    rc = _load().oracle_decode_tile_range(kind, _ptr(ln), _ptr(bs), bs.size, _ptr(gaps), _ptr(to),
+                                          int(b0), int(b1), int(c["n_threads"]), _ptr(sm),
+                                          ctypes.c_void_p(base))
     if rc != 0:
         raise ValueError("undecodable stream")
     return out

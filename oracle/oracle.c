@@ -672,6 +672,32 @@ int oracle_decode_tiles(int kind, const uint8_t *lengths, const uint8_t *stream,
   return status;
 }
 
+/* Decode tiles [b0, b1) only, single-threaded, into dst (which receives
+ * elements tile_out[b0] .. tile_out[b1] - 1 at those same indices).  The
+ * same range walk as oracle_decode_tiles, for sampled checks of very large
+ * containers. */
+int oracle_decode_tile_range(int kind, const uint8_t *lengths, const uint8_t *stream,
+                             uint64_t stream_bytes, const uint8_t *gaps,
+                             const uint64_t *tile_out, uint64_t b0, uint64_t b1,
+                             uint64_t n_threads, const uint8_t *sm, void *dst) {
+  canon_t c;
+  if (canon_init(lengths, &c) != 0) return -1;
+  range_job j;
+  j.kind = kind;
+  j.c = &c;
+  j.stream = stream;
+  j.stream_bytes = stream_bytes;
+  j.gaps = gaps;
+  j.tile_out = tile_out;
+  j.n_threads = n_threads;
+  j.sm = sm;
+  j.dst = dst;
+  j.b0 = b0;
+  j.b1 = b1;
+  range_worker(&j);
+  return j.status;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Checker for the multi-code decode table that the product library derives
  * from the lengths (a decoder-side accelerator; the pages' own tables are the

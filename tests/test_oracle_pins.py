@@ -468,3 +468,14 @@ def test_dtab_checker(orc, kind):
     bad[5] ^= np.uint64(1 << 56)
     bad[200] ^= np.uint64(1)
     assert orc.check_dtab(kind, ln, bad, K) == 2
+
+
+def test_tile_range_decode_matches_whole(orc):
+    rng = np.random.default_rng(21)
+    src = bf16_from_f32(rng.normal(0, 0.02, 200_000))
+    c = orc.compress(0, src)
+    nt = int(c["n_tiles"])
+    for b0, b1 in ((0, 1), (3, 7), (nt - 2, nt), (0, nt)):
+        part = orc.decode_tile_range(c, b0, b1)
+        lo, hi = int(c["tile_out"][b0]), int(c["tile_out"][b1])
+        assert np.array_equal(part, src[lo:hi])
