@@ -281,10 +281,12 @@ void decode_kernel(const Batch batch) {
     const uint64_t tile = base + grp;  // wave-uniform
     const bool active = tile < jb.n_tiles;
     const ChunkRegs cur = nxt;
-    uint64_t lo = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 0) << 32) |
-                  __builtin_amdgcn_readlane((uint32_t)nto, 0);
-    uint64_t hi = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 1) << 32) |
-                  __builtin_amdgcn_readlane((uint32_t)nto, 1);
+    // (readlane returns a signed int: widen through uint32_t, or offsets
+    // with bit 31 set would sign-extend)
+    uint64_t lo = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 0) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((uint32_t)nto, 0);
+    uint64_t hi = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 1) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((uint32_t)nto, 1);
     // take this step's stream words now, while nothing newer is in flight
     // (the memory counter retires in order), then put the next step's
     // words and offsets in flight

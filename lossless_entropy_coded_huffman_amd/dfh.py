@@ -188,17 +188,21 @@ def df_container_info(c: Container) -> dict:
 _SEC_DTYPE = {SEC_TILE_OUT: np.uint64, SEC_LUT: np.uint16, SEC_DTAB: np.uint64}
 
 
-def df_container_section(c: Container, sec) -> np.ndarray:
-    """Read-only numpy view of a section, valid while the container lives."""
-    if isinstance(sec, str):
-        sec = SECTION_NAMES.index(sec)
+def _section_bytes(c: Container, sec: int) -> np.ndarray:
+    """uint8 view of a section's bytes in library memory (no copy)."""
     nbytes = ctypes.c_uint64(0)
     ptr = lib().df_container_section(c.handle, int(sec), ctypes.byref(nbytes))
     if ptr is None:
         raise DFError(-1, "df_container_section")
     raw = (ctypes.c_uint8 * max(int(nbytes.value), 1)).from_address(ptr)
-    arr = np.frombuffer(raw, np.uint8, count=int(nbytes.value))
-    arr = arr.view(_SEC_DTYPE.get(int(sec), np.uint8))
+    return np.frombuffer(raw, np.uint8, count=int(nbytes.value))
+
+
+def df_container_section(c: Container, sec) -> np.ndarray:
+    """Read-only numpy view of a section, valid while the container lives."""
+    if isinstance(sec, str):
+        sec = SECTION_NAMES.index(sec)
+    arr = _section_bytes(c, int(sec)).view(_SEC_DTYPE.get(int(sec), np.uint8))
     arr.flags.writeable = False
     # keep the container alive as long as the view
     return _Owned(arr, c)
@@ -251,10 +255,10 @@ class DeviceContainer:
         self.device = torch.device(device)
         self.sections = {}
         for i, name in enumerate(SECTION_NAMES):
-            host = np.asarray(c.section(i)).view(np.uint8)
+            host = _section_bytes(c, i)
             t = torch.empty(max(host.size, 16), dtype=torch.uint8, device=self.device)
             if host.size:
-                t[: host.size].copy_(torch.from_numpy(np.array(host)), non_blocking=False)
+                t[: host.size].copy_(torch.from_numpy(host), non_blocking=False)
             self.sections[name] = t
         v = df_device_view()
         v.kind = self.kind

@@ -276,3 +276,22 @@ def test_llama3_8b_block_u8(torch_dev, orc):
         assert torch.equal(o, torch.from_numpy(q).to(dev))
     got = host_of(outs[4], 1)
     assert np.array_equal(got, orc.decode_tiles(oracle_container(cs[4]), 16))
+
+
+def test_offsets_beyond_2_pow_31(torch_dev):
+    """Element indices and tile offsets at and above 2^31 (uint8, two symbols,
+    one-bit codes: 2^31 + 2^20 + 37 weights, 2.2 GB)."""
+    torch, dev = torch_dev
+    n = (1 << 31) + (1 << 20) + 37
+    src = np.zeros(n, np.uint8)
+    src[1::3] = 200
+    src[n - 5:] = 200
+    c = dfh.compress(1, src)
+    assert int(np.asarray(c.section("tile_out"))[-2]) > (1 << 31)
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dfh.df_decompress_checked(dc, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(out, torch.from_numpy(src).to(dev))
