@@ -55,9 +55,11 @@
  *   DTAB           uint64[4096], derived from lengths, not stored in files:
  *                  a decoder-side table indexed by the next 12 stream bits
  *                  that gives up to five whole codes at once.  Layout:
- *                  bits 0..39 symbol bytes (BF16: exponent rotated right by
- *                  one bit), 40..51 start mask, 56..59 bits consumed, 60..63
- *                  number of codes (0 = first code longer than 12 bits).
+ *                  bits 0..31 symbol bytes of codes 0..3 (BF16: exponent
+ *                  rotated right by one bit), 32..36 bits consumed, 37..47
+ *                  flags for codes starting at window bits 1..11, 48..55
+ *                  symbol byte of code 4, 56..63 number of codes; 0 = first
+ *                  code longer than 12 bits.
  * n_threads = floor(start of last code / 64) + 1 (0 when n == 0) and
  * n_tiles = ceil(n_threads / 256).
  */

@@ -51,6 +51,9 @@ constexpr uint32_t kK = DF_DTAB_BITS;           // multi-code table index width
 constexpr uint32_t kDtabEntries = 1u << kK;
 constexpr uint32_t kDtabBytes = kDtabEntries * 8;
 constexpr uint32_t kPrefetch = 4;  // sign|mantissa 8-byte groups requested ahead per lane
+// s_waitcnt operand (gfx9 encoding: vmcnt in bits 3..0 and 15..14, expcnt
+// in 6..4, lgkmcnt in 11..8) that waits for vmcnt 0 only
+constexpr int kWaitVm0 = 0x0F70;
 // staging bytes past a tile's last element that phase 2 may touch: up to four
 // lookahead symbol bytes, widened to the two words of one OR
 constexpr uint32_t kSlack = 12;
@@ -75,14 +78,6 @@ struct Batch {
   uint32_t pad;
   uint32_t *err;       // error word (checked launches only)
 };
-
-// Stream bits [p, p + 32) of the 96-bit window w2:w1:w0, for p < 64.
-__device__ __forceinline__ uint32_t window(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t p) {
-  const bool up = p >= 32;
-  const uint32_t lo = up ? w1 : w0;
-  const uint32_t hi = up ? w2 : w1;
-  return (uint32_t)((((uint64_t)hi << 32) | lo) >> (p & 31));
-}
 
 // LDS is addressed through address-space-3 pointers made from byte offsets:
 // the kernel declares no static LDS, so its dynamic LDS starts at offset 0
@@ -146,48 +141,50 @@ __device__ __forceinline__ uint2 merge4(uint32_t e4, uint32_t s4) {
   return make_uint2((x0 & 0x7F7F7F7Fu) | (y0 & 0x80808080u), (x1 & 0x7F7F7F7Fu) | (y1 & 0x80808080u));
 }
 
-// Phase-1 lookup at chunk bit p: adds the number of the entry's codes that
-// start before the chunk end E (bits [8, 8 + min(E - p, 12)) of the entry's
-// high word are its start mask) and returns the bits the entry consumes.
-template <bool CHECKED>
-__device__ __forceinline__ uint32_t count_step(uint32_t n_luts, uint32_t win, uint32_t rem, uint32_t *err,
-                                               uint32_t &cnt) {
-  uint32_t h = lds<const lds_u32>(4)[(win & (kDtabEntries - 1)) << 1];
-  uint32_t adv = (h >> 24) & 15;
-  if (adv == 0) {
-    adv = long_code<CHECKED>(n_luts, win, err) >> 8;
-    h = 1u << 8;
-  }
-  cnt += __popc(__builtin_amdgcn_ubfe(h, 8, rem < kK ? rem : kK));
-  return adv;
+// A lane's position in its stream words: b2:b1:b0 holds the stream from
+// the current code on (bit 0 of b0 = first bit of the next code).  Built
+// from the chunk's three words w2:w1:w0 and the bit g (< 32) at which the
+// chunk's first code starts, it keeps every bit a lane reads: codes start
+// before chunk bit 64 and are at most 32 bits long.
+struct Stream {
+  uint32_t b0, b1, b2;
+};
+
+__device__ __forceinline__ Stream stream_at(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t g) {
+  return {__builtin_amdgcn_alignbit(w1, w0, g), __builtin_amdgcn_alignbit(w2, w1, g), w2 >> g};
 }
 
-// Phase-2 lookup: ORs the symbol bytes of the entry's codes into the staging
-// buffer at LDS byte q, advances q and returns the bits the entry consumes.
-// No clipping at the chunk end: codes of a lane's last lookup that start
-// past its chunk are the next lane's first codes (code boundaries are a
-// property of the stream), written to the same positions with the same
-// values by that lane, so the OR is idempotent; past the tile's last code
-// they land in the staging slack, which is never stored.
+// Drops the next (s mod 32) bits; s is a table entry's high word, whose
+// low five bits are the bits its codes consume (1..12).
+__device__ __forceinline__ void drop(Stream &t, uint32_t s) {
+  t.b0 = __builtin_amdgcn_alignbit(t.b1, t.b0, s);
+  t.b1 = __builtin_amdgcn_alignbit(t.b2, t.b1, s);
+  t.b2 = t.b2 >> (s & 31);
+}
+
+// Multi-code table entry fields (high word): bits consumed in bits 0..4,
+// flags for codes starting at window bits 1..11 in bits 5..15, the fifth
+// symbol byte in bits 16..23, the number of codes in bits 24..31; a high
+// word below 2^24 marks a first code longer than the table's index width.
+constexpr uint32_t kOneCode = 1u << 24;
+
+// In place of a table entry whose first code is longer than the index width:
+// an entry for that one code (symbol byte in the low word for phase 2).  A
+// 32-bit code, whose length does not fit the five-bit field, drops one
+// stream word here and reports 0 bits (phase 1 takes the 32 bits off its
+// budget itself).
 template <int KIND, bool CHECKED>
-__device__ __forceinline__ uint32_t decode_step(uint32_t n_luts, uint32_t win, uint32_t *err, uint32_t &q) {
-  const v2u e = lds<const lds_v2>(0)[win & (kDtabEntries - 1)];
-  uint32_t adv = (e.y >> 24) & 15;
-  uint32_t nc = e.y >> 28;
-  uint32_t s0 = e.x, s1 = e.y & 0xFFu;
-  if (adv == 0) {  // rare: a code longer than the table's index width
-    const uint32_t c = long_code<CHECKED>(n_luts, win, err);
-    adv = c >> 8;
-    s0 = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
-    s1 = 0;
-    nc = 1;
+__device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
+  const uint32_t c = long_code<CHECKED>(n_luts, t.b0, err);
+  uint32_t len = c >> 8;
+  if (len >= 32) {
+    t.b0 = t.b1;
+    t.b1 = t.b2;
+    t.b2 = 0;
+    len = 0;
   }
-  const uint64_t v = ((((uint64_t)s1) << 32) | s0) << ((q & 3) * 8);
-  lds_u32 *w = lds<lds_u32>(q & ~3u);
-  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  q += nc;
-  return adv;
+  const uint32_t sym = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+  return (v2u){sym, kOneCode | len};
 }
 
 // Element-wise stores of the part of a 16-byte store granule that lies in
@@ -205,6 +202,59 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
   for (uint32_t i = 0; i < 16; i++) {
     const uint32_t w = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
     if (e0 + i >= lo && e0 + i < hi) dst[e0 + i] = (uint8_t)(w >> (8 * (i & 3)));
+  }
+}
+
+// The store pass of one tile: aligned 16-byte stores of output elements
+// [a + lo_r, a + hi_r) from the staging buffer at LDS byte buf; BF16 merges
+// each granule's exponents with its sign|mantissa bytes (the first
+// kPrefetch granules of each lane arrive in smv, the rest are loaded here).
+// A BF16 lane keeps one store in flight: it waits for the previous store
+// (s_waitcnt vmcnt(0); no load is outstanding here) before the next.  When
+// every wave issued its stores back to back, the write bursts delayed the
+// stream and sign|mantissa loads that the decode waits on, and the kernel
+// ran about 5% slower.
+template <int KIND>
+__device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t a, uint32_t lo_r,
+                                           uint32_t hi_r, uint32_t ngroups, const uint2 (&smv)[kPrefetch],
+                                           uint32_t lane) {
+  if (KIND == DF_KIND_BF16) {
+    uint16_t *dst_t = (uint16_t *)jb.dst + a;
+    const uint8_t *sm_t = jb.sm + a;
+    const lds_v2 *ex_t = lds<const lds_v2>(buf);
+#pragma unroll
+    for (uint32_t k = 0; k < kPrefetch; k++) {
+      const uint32_t g = lane + k * kTPB;
+      if (k > 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (g < ngroups) {
+        const uint32_t e0 = 8 * g;
+        const v2u ex = ex_t[g];
+        const uint2 o01 = merge4(ex.x, smv[k].x);
+        const uint2 o23 = merge4(ex.y, smv[k].y);
+        const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
+        if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
+        else store_partial(dst_t, e0, lo_r, hi_r, o);
+      }
+    }
+    for (uint32_t g = lane + kPrefetch * kTPB; g < ngroups; g += kTPB) {
+      const uint32_t e0 = 8 * g;
+      const v2u ex = ex_t[g];
+      const uint2 sv = *(const uint2 *)(sm_t + e0);
+      const uint2 o01 = merge4(ex.x, sv.x);
+      const uint2 o23 = merge4(ex.y, sv.y);
+      const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
+      if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
+      else store_partial(dst_t, e0, lo_r, hi_r, o);
+    }
+  } else {
+    uint8_t *dst_t = (uint8_t *)jb.dst + a;
+    const lds_v4 *ex_t = lds<const lds_v4>(buf);
+    for (uint32_t g = lane; g < ngroups; g += kTPB) {
+      const uint32_t e0 = 16 * g;
+      const v4u v = ex_t[g];
+      if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
+      else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
+    }
   }
 }
 
@@ -233,7 +283,7 @@ template <int KIND, bool CHECKED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
   // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
-  // one staging buffer per tile group, then the per-wave scan sums
+  // two staging buffers per tile group, then the per-wave scan sums
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
@@ -243,8 +293,9 @@ void decode_kernel(const Batch batch) {
   const uint32_t grp = __builtin_amdgcn_readfirstlane(tid / kTPB);
   const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
-  const uint32_t out_base = kDtabBytes + batch.lut_bytes + grp * batch.out_bytes;  // LDS byte offset
-  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * batch.out_bytes);
+  const uint32_t out_bytes = batch.out_bytes;
+  const uint32_t buf0 = kDtabBytes + batch.lut_bytes + grp * 2 * out_bytes;  // LDS byte offset
+  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * 2 * out_bytes);
 
   {  // stage the tables once per workgroup: the first four 16-byte words per
      // lane (all a 1024-lane workgroup needs for up to 64 levels) with every
@@ -277,7 +328,15 @@ void decode_kernel(const Batch batch) {
   if (base + grp < jb.n_tiles) nto = jb.tile_out[base + grp + (lane & 1)];
   __syncthreads();
 
-  for (; base < jb.n_tiles; base += step) {
+  // The previous tile of this group is stored one step late, from the other
+  // staging buffer, while this step counts: the store pass (HBM-heavy) then
+  // shares a barrier interval with phase 1 (LDS- and ALU-heavy).
+  bool have_prev = false;
+  uint64_t prev_a = 0;
+  uint32_t prev_lo = 0, prev_hi = 0, prev_ng = 0;
+  uint32_t parity = 0;
+
+  for (; base < jb.n_tiles; base += step, parity ^= 1) {
     const uint64_t tile = base + grp;  // wave-uniform
     const bool active = tile < jb.n_tiles;
     const ChunkRegs cur = nxt;
@@ -293,6 +352,15 @@ void decode_kernel(const Batch batch) {
     asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
     nxt = load_chunk(jb, tile + step, lane);
     if (tile + step < jb.n_tiles) nto = jb.tile_out[tile + step + (lane & 1)];
+    // request the previous tile's first sign|mantissa granules; they are
+    // used by its store pass after this tile's count
+    uint2 smv[kPrefetch];
+#pragma unroll
+    for (uint32_t k = 0; k < kPrefetch; k++) {
+      const uint32_t g = lane + k * kTPB;
+      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * g)
+                                                    : make_uint2(0, 0);
+    }
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
     if (hi - lo > jb.max_tile_elems) hi = lo + jb.max_tile_elems;
@@ -301,17 +369,8 @@ void decode_kernel(const Batch batch) {
     const uint32_t lo_r = (uint32_t)(lo - a), hi_r = (uint32_t)(hi - a);
     const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : 16u;  // elements per store granule
     const uint32_t ngroups = active ? (hi_r + gsz - 1) / gsz : 0u;
-
-    // this tile's sign|mantissa bytes go in flight before decoding
-    uint2 smv[kPrefetch];
-    const uint8_t *sm_t = jb.sm + a;
-    if (KIND == DF_KIND_BF16) {
-#pragma unroll
-      for (uint32_t k = 0; k < kPrefetch; k++) {
-        const uint32_t g = lane + k * kTPB;
-        smv[k] = g < ngroups ? *(const uint2 *)(sm_t + 8 * g) : make_uint2(0, 0);
-      }
-    }
+    const uint32_t bufc = buf0 + parity * out_bytes;        // this tile's staging
+    const uint32_t bufp = buf0 + (parity ^ 1) * out_bytes;  // the previous tile's
 
     // chunk bounds: codes start in [gap, E) of this lane's 64 stream bits
     uint32_t gap = 0, E = 0;
@@ -333,14 +392,47 @@ void decode_kernel(const Batch batch) {
     // last lane's lookahead codes
     if (active) {
       const uint32_t zero_bytes = (hi_r + kSlack + 15) & ~15u;
-      lds_v4 *z = lds<lds_v4>(out_base);
+      lds_v4 *z = lds<lds_v4>(bufc);
       for (uint32_t i = lane; i < zero_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
     }
 
-    // phase 1: count the codes that start in [gap, E)
+    // phase 1: count the codes that start in [gap, E).  Whole entries are
+    // counted; the entry that crosses E gives back its codes that start at
+    // or past E (they are the next lane's first codes).
     uint32_t cnt = 0;
-    for (uint32_t p = gap; p < E;)
-      p += count_step<CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), E - p, batch.err, cnt);
+    {
+      Stream t = stream_at(cur.w0, cur.w1, cur.w2, gap);
+      int32_t rem = (int32_t)(E - gap);  // bits left before E
+      uint32_t h = 0;
+      while (rem > 0) {
+        h = lds<const lds_u32>(4)[(t.b0 & (kDtabEntries - 1)) << 1];
+        if (h < kOneCode) {  // rare: a code longer than the table's index width
+          h = long_entry<KIND, CHECKED>(n_luts, t, batch.err).y;
+          if ((h & 31) == 0) rem -= 32;
+        }
+        drop(t, h);
+        rem -= (int32_t)(h & 31);
+        cnt += h >> 24;
+      }
+      if (rem < 0) {
+        // bits of the last entry before E (1..11; a one-code entry has no flags)
+        const uint32_t r = (uint32_t)(rem + (int32_t)(h & 31));
+        cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
+      }
+    }
+
+    // store the previous tile.  Its sign|mantissa registers are taken here,
+    // once and on every path, so the store pass starts with no load in
+    // flight and no later reuse of the registers waits behind the chunk
+    // prefetch.
+#pragma unroll
+    for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
+    if (have_prev) store_tile<KIND>(jb, bufp, prev_a, prev_lo, prev_hi, prev_ng, smv, lane);
+    have_prev = active;
+    prev_a = a;
+    prev_lo = lo_r;
+    prev_hi = hi_r;
+    prev_ng = ngroups;
 
     // prefix sum of the counts over the tile's 256 lanes
     const uint32_t wid = tid >> 6;
@@ -354,59 +446,48 @@ void decode_kernel(const Batch batch) {
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
 
-    // phase 2: decode again, OR the symbol bytes into the staging buffer.
-    // A lane whose codes would not fit the buffer (only with corrupt offsets
-    // or stream) skips the phase, so LDS writes stay inside the buffer.
+    // phase 2: decode again and OR the symbol bytes into the staging buffer
+    // until the lane's cnt codes are written.  The entry that crosses the
+    // chunk end is not clipped: its codes past the end are the next lane's
+    // first codes (code boundaries are a property of the stream), written to
+    // the same positions with the same values by that lane, so the OR is
+    // idempotent; past the tile's last code they land in the staging slack,
+    // which is never stored.  A lane whose codes would not fit the buffer
+    // (only with corrupt offsets or stream) skips the phase, so LDS writes
+    // stay inside the buffer.
     {
-      uint32_t q = out_base + lo_r + off;
-      uint32_t end = E;
-      if (lo_r + off + cnt + kSlack > batch.out_bytes) {
-        end = 0;
+      uint32_t q = bufc + lo_r + off;
+      uint32_t qend = q + cnt;
+      if (lo_r + off + cnt + kSlack > out_bytes) {
+        qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
       }
-      for (uint32_t p = gap; p < end;)
-        p += decode_step<KIND, CHECKED>(n_luts, window(cur.w0, cur.w1, cur.w2, p), batch.err, q);
+      Stream t = stream_at(cur.w0, cur.w1, cur.w2, gap);
+      while (q < qend) {
+        v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+        if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, batch.err);  // rare
+        drop(t, e.y);
+        const uint64_t v = ((((uint64_t)((e.y >> 16) & 0xFFu)) << 32) | e.x) << ((q & 3) * 8);
+        lds_u32 *w = lds<lds_u32>(q & ~3u);
+        __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        q += e.y >> 24;
+      }
     }
     __syncthreads();
-
-    // one coalesced pass: aligned 16-byte stores of the tile's output range
-    if (KIND == DF_KIND_BF16) {
-      uint16_t *dst_t = (uint16_t *)jb.dst + a;
-      const lds_v2 *ex_t = lds<const lds_v2>(out_base);
+  }
+  // the last tile of this group
+  if (have_prev) {
+    uint2 smv[kPrefetch];
 #pragma unroll
-      for (uint32_t k = 0; k < kPrefetch; k++) {
-        const uint32_t g = lane + k * kTPB;
-        if (g < ngroups) {
-          const uint32_t e0 = 8 * g;
-          const v2u ex = ex_t[g];
-          const uint2 o01 = merge4(ex.x, smv[k].x);
-          const uint2 o23 = merge4(ex.y, smv[k].y);
-          const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
-          if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
-          else store_partial(dst_t, e0, lo_r, hi_r, o);
-        }
-      }
-      for (uint32_t g = lane + kPrefetch * kTPB; g < ngroups; g += kTPB) {
-        const uint32_t e0 = 8 * g;
-        const v2u ex = ex_t[g];
-        const uint2 sv = *(const uint2 *)(sm_t + e0);
-        const uint2 o01 = merge4(ex.x, sv.x);
-        const uint2 o23 = merge4(ex.y, sv.y);
-        const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
-        if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
-        else store_partial(dst_t, e0, lo_r, hi_r, o);
-      }
-    } else {
-      uint8_t *dst_t = (uint8_t *)jb.dst + a;
-      const lds_v4 *ex_t = lds<const lds_v4>(out_base);
-      for (uint32_t g = lane; g < ngroups; g += kTPB) {
-        const uint32_t e0 = 16 * g;
-        const v4u v = ex_t[g];
-        if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
-        else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
-      }
+    for (uint32_t k = 0; k < kPrefetch; k++) {
+      const uint32_t g = lane + k * kTPB;
+      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * g)
+                                                    : make_uint2(0, 0);
     }
-    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
+    store_tile<KIND>(jb, buf0 + (parity ^ 1) * out_bytes, prev_a, prev_lo, prev_hi, prev_ng, smv, lane);
   }
 }
 
@@ -515,8 +596,8 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     uint32_t groups = 0;
     int per_cu = 0;
     size_t lds = 0;
-    for (uint32_t g = kMaxGroups; g >= 1; g /= 2) {
-      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes + 16 * g;
+    for (uint32_t g = kMaxGroups; g >= 1; g--) {
+      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * 2 * out_bytes + 16 * g;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=

@@ -278,7 +278,10 @@ void build_dtab(df_kind kind, const std::vector<uint16_t> &lut, std::vector<uint
       pos += l;
       count++;
     }
-    if (count) dtab[w] = syms | (starts << 40) | ((uint64_t)pos << 56) | ((uint64_t)count << 60);
+    // symbols 0..3 | consumed bits | start flags for bits 1..11 | symbol 4 | count
+    if (count)
+      dtab[w] = (syms & 0xFFFFFFFFull) | ((uint64_t)pos << 32) | ((starts >> 1) << 37) | ((syms >> 32) << 48) |
+                ((uint64_t)count << 56);
   }
 }
 

@@ -704,15 +704,19 @@ int oracle_decode_tile_range(int kind, const uint8_t *lengths, const uint8_t *st
  * hierarchical ones above).  Entry w (0 <= w < 2^K) describes the stream
  * whose next K bits are w (first bit = bit 0 of w): the codes that lie
  * entirely inside those K bits, at most five, are decoded in order.  u64
- * entry layout:
- *   bits  0..39  symbol bytes, code i in byte i, unused bytes zero; for the
- *                BF16 kind the byte is the exponent rotated right by one bit
- *                ((e >> 1) | (e & 1) << 7), for uint8 the symbol itself;
- *   bits 40..51  start mask: bit j set when one of the codes starts at bit j;
- *   bits 52..55  zero;
- *   bits 56..59  bits consumed by the codes (sum of their lengths);
- *   bits 60..63  number of codes (0 = the first code is longer than K bits,
- *                or no code has this prefix).
+ * entry layout (fields placed so the decoder reads each with one operation):
+ *   bits  0..31  symbol bytes of codes 0..3, code i in byte i, unused bytes
+ *                zero; for the BF16 kind the byte is the exponent rotated
+ *                right by one bit ((e >> 1) | (e & 1) << 7), for uint8 the
+ *                symbol itself;
+ *   bits 32..36  bits consumed by the codes (sum of their lengths);
+ *   bits 37..47  start flags: bit 37 + (j - 1) set when one of the codes
+ *                starts at window bit j, for j = 1..11 (the first code
+ *                always starts at bit 0);
+ *   bits 48..55  symbol byte of code 4 (zero when there are fewer codes);
+ *   bits 56..63  number of codes.
+ * The entry is zero when the first code is longer than K bits or no code
+ * has this prefix.
  * Returns the number of entries that differ from this definition.           */
 /* ------------------------------------------------------------------------ */
 int64_t oracle_check_dtab(int kind, const uint8_t *lengths, const uint64_t *dtab,
@@ -747,7 +751,8 @@ int64_t oracle_check_dtab(int kind, const uint8_t *lengths, const uint64_t *dtab
       used += (uint64_t)len;
       ncodes++;
     }
-    uint64_t expect = syms | (mask << 40) | (used << 56) | (ncodes << 60);
+    uint64_t expect = (syms & 0xFFFFFFFFull) | (used << 32) | ((mask >> 1) << 37) |
+                      ((syms >> 32) << 48) | (ncodes << 56);
     if (ncodes == 0) expect = 0;
     if (dtab[w] != expect) bad++;
   }

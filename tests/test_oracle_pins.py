@@ -449,9 +449,9 @@ def python_dtab(kind, lengths, codes, K):
         v = 0
         for i, s in enumerate(syms):
             byte = ((s >> 1) | ((s & 1) << 7)) if kind == 0 else s
-            v |= byte << (8 * i)
-        mask = sum(1 << st for st in starts)
-        v |= mask << 40 | pos << 56 | len(syms) << 60
+            v |= byte << (8 * i if i < 4 else 48)
+        flags = sum(1 << (st - 1) for st in starts if st > 0)
+        v |= pos << 32 | flags << 37 | len(syms) << 56
         tab[w] = v
     return tab
 
