@@ -88,6 +88,9 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) v2u lds_v2;
 typedef __attribute__((address_space(3))) v4u lds_v4;
+// tile offsets are wave-uniform and read through the constant address
+// space, which makes them scalar loads
+typedef const __attribute__((address_space(4))) uint64_t k_u64;
 template <class T>
 __device__ __forceinline__ T *lds(uint32_t byte_offset) {
   return (T *)(uintptr_t)byte_offset;
@@ -264,18 +267,20 @@ struct ChunkRegs {
 
 // The stream words and gap fields of one lane of a tile.  Addresses are a
 // wave-uniform base plus a 32-bit lane offset.
+// A tile past the last (a group with no next tile) reads the last tile
+// again: the loads are issued on every path, so each step puts the same
+// number of loads in flight, in the same order.  Needs n_tiles >= 1.
 __device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, uint32_t lane) {
-  ChunkRegs c = {0u, 0u, 0u, 0u, 0u};
-  if (tile < jb.n_tiles) {
-    const uint32_t *bits_t = jb.bits + tile * (2 * kTPB);
-    const uint2 w01 = *(const uint2 *)(bits_t + 2 * lane);
-    c.w0 = w01.x;
-    c.w1 = w01.y;
-    c.w2 = bits_t[2 * lane + 2];
-    const uint32_t *gaps_t = jb.gaps + tile * (5 * kTPB / 32);  // 1280 bits per tile
-    c.g0 = gaps_t[(5 * lane) >> 5];
-    c.g1 = gaps_t[((5 * lane) >> 5) + 1];
-  }
+  if (tile >= jb.n_tiles) tile = jb.n_tiles - 1;
+  ChunkRegs c;
+  const uint32_t *bits_t = jb.bits + tile * (2 * kTPB);
+  const uint2 w01 = *(const uint2 *)(bits_t + 2 * lane);
+  c.w0 = w01.x;
+  c.w1 = w01.y;
+  c.w2 = bits_t[2 * lane + 2];
+  const uint32_t *gaps_t = jb.gaps + tile * (5 * kTPB / 32);  // 1280 bits per tile
+  c.g0 = gaps_t[(5 * lane) >> 5];
+  c.g1 = gaps_t[((5 * lane) >> 5) + 1];
   return c;
 }
 
@@ -321,11 +326,13 @@ void decode_kernel(const Batch batch) {
   const uint64_t step = (uint64_t)jb.wg_count * groups;
   uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
   ChunkRegs nxt = load_chunk(jb, base + grp, lane);
-  // a tile's first and last output index: lane 0 of each wave loads
-  // tile_out[t], lane 1 tile_out[t + 1]; kept in vector registers until the
-  // step that uses them
-  uint64_t nto = 0;
-  if (base + grp < jb.n_tiles) nto = jb.tile_out[base + grp + (lane & 1)];
+  // the next tile's first and last output index, one step ahead
+  k_u64 *tout = (k_u64 *)jb.tile_out;
+  uint64_t nlo = 0, nhi = 0;
+  if (base + grp < jb.n_tiles) {
+    nlo = tout[base + grp];
+    nhi = tout[base + grp + 1];
+  }
   __syncthreads();
 
   // The previous tile of this group is stored one step late, from the other
@@ -339,27 +346,27 @@ void decode_kernel(const Batch batch) {
   for (; base < jb.n_tiles; base += step, parity ^= 1) {
     const uint64_t tile = base + grp;  // wave-uniform
     const bool active = tile < jb.n_tiles;
-    const ChunkRegs cur = nxt;
-    // (readlane returns a signed int: widen through uint32_t, or offsets
-    // with bit 31 set would sign-extend)
-    uint64_t lo = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 0) << 32) |
-                  (uint32_t)__builtin_amdgcn_readlane((uint32_t)nto, 0);
-    uint64_t hi = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(nto >> 32), 1) << 32) |
-                  (uint32_t)__builtin_amdgcn_readlane((uint32_t)nto, 1);
-    // take this step's stream words now, while nothing newer is in flight
-    // (the memory counter retires in order), then put the next step's
-    // words and offsets in flight
-    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
-    nxt = load_chunk(jb, tile + step, lane);
-    if (tile + step < jb.n_tiles) nto = jb.tile_out[tile + step + (lane & 1)];
-    // request the previous tile's first sign|mantissa granules; they are
-    // used by its store pass after this tile's count
+    // The previous tile's first sign|mantissa granules go in flight first
+    // (granules past the tile read its last one; step 0 reads granule 0),
+    // then the wait for this step's stream words leaves exactly these loads
+    // outstanding (the memory counter retires in order), then the next
+    // step's words go in flight.
     uint2 smv[kPrefetch];
+    if (KIND == DF_KIND_BF16) {
+      const uint64_t last = prev_ng ? prev_a + 8 * (uint64_t)(prev_ng - 1) : 0;
 #pragma unroll
-    for (uint32_t k = 0; k < kPrefetch; k++) {
-      const uint32_t g = lane + k * kTPB;
-      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * g)
-                                                    : make_uint2(0, 0);
+      for (uint32_t k = 0; k < kPrefetch; k++) {
+        const uint32_t g = lane + k * kTPB;
+        smv[k] = *(const uint2 *)(jb.sm + (g < prev_ng ? prev_a + 8 * (uint64_t)g : last));
+      }
+    }
+    const ChunkRegs cur = nxt;
+    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
+    uint64_t lo = nlo, hi = nhi;
+    nxt = load_chunk(jb, tile + step, lane);
+    if (tile + step < jb.n_tiles) {
+      nlo = tout[tile + step];
+      nhi = tout[tile + step + 1];
     }
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
@@ -422,9 +429,8 @@ void decode_kernel(const Batch batch) {
     }
 
     // store the previous tile.  Its sign|mantissa registers are taken here,
-    // once and on every path, so the store pass starts with no load in
-    // flight and no later reuse of the registers waits behind the chunk
-    // prefetch.
+    // once and on every path: the wait leaves the next step's stream words
+    // in flight, and the store pass starts with no other load outstanding.
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
     if (have_prev) store_tile<KIND>(jb, bufp, prev_a, prev_lo, prev_hi, prev_ng, smv, lane);
@@ -482,7 +488,7 @@ void decode_kernel(const Batch batch) {
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) {
       const uint32_t g = lane + k * kTPB;
-      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * g)
+      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * (uint64_t)g)
                                                     : make_uint2(0, 0);
     }
 #pragma unroll
