@@ -217,14 +217,22 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
 // every wave issued its stores back to back, the write bursts delayed the
 // stream and sign|mantissa loads that the decode waits on, and the kernel
 // ran about 5% slower.
+//
+// The pass also leaves the staging buffer zero for the next tile's ORs:
+// each lane clears the granules it has just read, and the bytes from the
+// last granule up to `dirty` (the next lane-group's lookahead slack) are
+// cleared here too.
 template <int KIND>
 __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t a, uint32_t lo_r,
-                                           uint32_t hi_r, uint32_t ngroups, const uint2 (&smv)[kPrefetch],
-                                           uint32_t lane) {
+                                           uint32_t hi_r, uint32_t ngroups, uint32_t dirty,
+                                           const uint2 (&smv)[kPrefetch], uint32_t lane) {
+  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : 16u;
+  for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
+    *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
   if (KIND == DF_KIND_BF16) {
     uint16_t *dst_t = (uint16_t *)jb.dst + a;
     const uint8_t *sm_t = jb.sm + a;
-    const lds_v2 *ex_t = lds<const lds_v2>(buf);
+    lds_v2 *ex_t = lds<lds_v2>(buf);
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) {
       const uint32_t g = lane + k * kTPB;
@@ -232,6 +240,7 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
       if (g < ngroups) {
         const uint32_t e0 = 8 * g;
         const v2u ex = ex_t[g];
+        ex_t[g] = (v2u){0u, 0u};
         const uint2 o01 = merge4(ex.x, smv[k].x);
         const uint2 o23 = merge4(ex.y, smv[k].y);
         const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
@@ -242,6 +251,7 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
     for (uint32_t g = lane + kPrefetch * kTPB; g < ngroups; g += kTPB) {
       const uint32_t e0 = 8 * g;
       const v2u ex = ex_t[g];
+      ex_t[g] = (v2u){0u, 0u};
       const uint2 sv = *(const uint2 *)(sm_t + e0);
       const uint2 o01 = merge4(ex.x, sv.x);
       const uint2 o23 = merge4(ex.y, sv.y);
@@ -251,10 +261,11 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
     }
   } else {
     uint8_t *dst_t = (uint8_t *)jb.dst + a;
-    const lds_v4 *ex_t = lds<const lds_v4>(buf);
+    lds_v4 *ex_t = lds<lds_v4>(buf);
     for (uint32_t g = lane; g < ngroups; g += kTPB) {
       const uint32_t e0 = 16 * g;
       const v4u v = ex_t[g];
+      ex_t[g] = (v4u){0u, 0u, 0u, 0u};
       if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
       else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
     }
@@ -288,7 +299,7 @@ template <int KIND, bool CHECKED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
   // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
-  // two staging buffers per tile group, then the per-wave scan sums
+  // one staging buffer per tile group, then the per-wave scan sums
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
@@ -299,8 +310,8 @@ void decode_kernel(const Batch batch) {
   const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
   const uint32_t out_bytes = batch.out_bytes;
-  const uint32_t buf0 = kDtabBytes + batch.lut_bytes + grp * 2 * out_bytes;  // LDS byte offset
-  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * 2 * out_bytes);
+  const uint32_t buf = kDtabBytes + batch.lut_bytes + grp * out_bytes;  // LDS byte offset
+  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * out_bytes);
 
   {  // stage the tables once per workgroup: the first four 16-byte words per
      // lane (all a 1024-lane workgroup needs for up to 64 levels) with every
@@ -333,17 +344,22 @@ void decode_kernel(const Batch batch) {
     nlo = tout[base + grp];
     nhi = tout[base + grp + 1];
   }
+  {  // the staging buffer starts zero (out_bytes is a multiple of 16)
+    lds_v4 *z = lds<lds_v4>(buf);
+    for (uint32_t i = lane; i < out_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
+  }
   __syncthreads();
 
-  // The previous tile of this group is stored one step late, from the other
-  // staging buffer, while this step counts: the store pass (HBM-heavy) then
-  // shares a barrier interval with phase 1 (LDS- and ALU-heavy).
+  // The previous tile of this group is stored one step late, while this
+  // step counts: the store pass (HBM-heavy) then shares a barrier interval
+  // with phase 1 (LDS- and ALU-heavy).  It reads the staging buffer before
+  // phase 2 writes it again (a barrier lies between) and clears what it
+  // reads, so one buffer per group suffices.
   bool have_prev = false;
   uint64_t prev_a = 0;
-  uint32_t prev_lo = 0, prev_hi = 0, prev_ng = 0;
-  uint32_t parity = 0;
+  uint32_t prev_lo = 0, prev_hi = 0, prev_ng = 0, prev_dirty = 0;
 
-  for (; base < jb.n_tiles; base += step, parity ^= 1) {
+  for (; base < jb.n_tiles; base += step) {
     const uint64_t tile = base + grp;  // wave-uniform
     const bool active = tile < jb.n_tiles;
     // The previous tile's first sign|mantissa granules go in flight first
@@ -376,8 +392,6 @@ void decode_kernel(const Batch batch) {
     const uint32_t lo_r = (uint32_t)(lo - a), hi_r = (uint32_t)(hi - a);
     const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : 16u;  // elements per store granule
     const uint32_t ngroups = active ? (hi_r + gsz - 1) / gsz : 0u;
-    const uint32_t bufc = buf0 + parity * out_bytes;        // this tile's staging
-    const uint32_t bufp = buf0 + (parity ^ 1) * out_bytes;  // the previous tile's
 
     // chunk bounds: codes start in [gap, E) of this lane's 64 stream bits
     uint32_t gap = 0, E = 0;
@@ -393,14 +407,6 @@ void decode_kernel(const Batch batch) {
           E = r < 64 ? r : 64u;
         }
       }
-    }
-
-    // clear the staging bytes this tile uses, plus the slack written by the
-    // last lane's lookahead codes
-    if (active) {
-      const uint32_t zero_bytes = (hi_r + kSlack + 15) & ~15u;
-      lds_v4 *z = lds<lds_v4>(bufc);
-      for (uint32_t i = lane; i < zero_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
     }
 
     // phase 1: count the codes that start in [gap, E).  Whole entries are
@@ -433,7 +439,7 @@ void decode_kernel(const Batch batch) {
     // in flight, and the store pass starts with no other load outstanding.
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    if (have_prev) store_tile<KIND>(jb, bufp, prev_a, prev_lo, prev_hi, prev_ng, smv, lane);
+    if (have_prev) store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_ng, prev_dirty, smv, lane);
     have_prev = active;
     prev_a = a;
     prev_lo = lo_r;
@@ -451,6 +457,10 @@ void decode_kernel(const Batch batch) {
     const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
+    {  // bytes phase 2 may write: every lane ends by lo_r + off + cnt + 7
+      const uint32_t d = (lo_r + s0 + s1 + s2 + s3 + kSlack + 7) & ~7u;
+      prev_dirty = d < out_bytes ? d : out_bytes;
+    }
 
     // phase 2: decode again and OR the symbol bytes into the staging buffer
     // until the lane's cnt codes are written.  The entry that crosses the
@@ -462,7 +472,7 @@ void decode_kernel(const Batch batch) {
     // (only with corrupt offsets or stream) skips the phase, so LDS writes
     // stay inside the buffer.
     {
-      uint32_t q = bufc + lo_r + off;
+      uint32_t q = buf + lo_r + off;
       uint32_t qend = q + cnt;
       if (lo_r + off + cnt + kSlack > out_bytes) {
         qend = q;
@@ -493,7 +503,7 @@ void decode_kernel(const Batch batch) {
     }
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    store_tile<KIND>(jb, buf0 + (parity ^ 1) * out_bytes, prev_a, prev_lo, prev_hi, prev_ng, smv, lane);
+    store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_ng, prev_dirty, smv, lane);
   }
 }
 
@@ -603,7 +613,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     int per_cu = 0;
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
-      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * 2 * out_bytes + 16 * g;
+      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes + 16 * g;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
