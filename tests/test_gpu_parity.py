@@ -225,6 +225,40 @@ def test_checked_reports_bad_tile_offsets(torch_dev):
     assert int(err.item()) & dfh.DEVERR_COUNT
 
 
+@pytest.mark.parametrize("checked", [True, False])
+def test_corrupt_tile_is_contained(torch_dev, checked):
+    # error path forced from the host: one lane's 64 stream bits in one tile
+    # are zeroed on the device (all-zero bits decode as the first, shortest
+    # canonical code over and over, so the tile's code count no longer
+    # matches its offsets).  Tiles share a tile group's staging buffer in
+    # turn (each group decodes several tiles here: more tiles than the GPU
+    # has group slots), so this checks that a corrupt tile leaves no bytes
+    # behind for the next one: every element outside the corrupt tile and
+    # the tile before it (whose last lane reads ahead into it) is exact.
+    torch, dev = torch_dev
+    src = bf16_normal(30_000_000, 12)
+    c = dfh.compress(0, src)
+    nt = int(c.info()["n_tiles"])
+    assert nt > 4096
+    to = np.asarray(c.section("tile_out")).astype(np.int64)
+    dc = dfh.to_device(c, dev)
+    t = nt // 3
+    bits = dc.sections["bitstream"].view(torch.int32)
+    bits[t * 512 + 200: t * 512 + 202] = 0
+    out = dc.empty_output()
+    if checked:
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        dfh.df_decompress_checked(dc, out, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) != 0
+    else:
+        dfh.df_decompress(dc, out)
+    got = host_of(out, 0)
+    lo, hi = int(to[t - 1]), int(to[t + 1])
+    assert np.array_equal(got[:lo], src[:lo])
+    assert np.array_equal(got[hi:], src[hi:])
+
+
 def test_rejects_bad_arguments(torch_dev):
     torch, dev = torch_dev
     dc = dfh.to_device(dfh.compress(0, bf16_normal(1000, 1)), dev)
