@@ -55,7 +55,7 @@ def algorithmic_bytes(inf) -> int:
 
 
 WORKLOADS = ("llama3_8b_block_bf16", "c1_1m_bf16", "llama3_8b_block_u8", "llama3_8b_32_blocks_bf16",
-             "llama31_405b_block_t3_bf16")
+             "llama31_405b_block_t3_bf16", "llama3_8b_lm_head_bf16")
 
 
 def make_workload(name: str, seed: int):
@@ -86,6 +86,10 @@ def make_workload(name: str, seed: int):
                                   dist="t3")
         return 0, [src], {"matrices": "q,k,v,o,gate,up,down", "shapes": "Llama-3.1-405B block",
                           "dist": "Student-t(3)*0.02/sqrt(3)"}, "one"
+    if name == "llama3_8b_lm_head_bf16":
+        src, _ = synth.bf16_block(seed, config=synth.CONFIG_LM_HEAD, shapes=synth.LLAMA3_8B_LM_HEAD)
+        return 0, [src], {"matrices": "lm_head", "shapes": "128256x4096, one matrix, one codebook",
+                          "dist": "N(0,s^2), s~U[0.01,0.04]"}, "one"
     raise SystemExit("unknown workload " + name)
 
 
@@ -131,7 +135,18 @@ def cpu_baseline(containers, srcs, kind):
                   "the first 1/16 of the first container's tiles (%d elements)"
                   % (keep, total, cores, d0["n"]),
         "value_1thread": round(d0["n"] * esz / t_1 / 1e9, 4), "verified": bool(ok),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -257,6 +272,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(alg), "launch_ms_mean": round(mean_ms, 5),
+                     "launch_ms_median": round(statistics.median(launch_ms), 5),
                      "launch_ms_min": round(min(launch_ms), 5)},
         "verified": verified,
     }

@@ -43,7 +43,10 @@ LLAMA31_405B_BLOCK = (
     ("gate", 53248, 16384), ("up", 53248, 16384), ("down", 16384, 53248),
 )
 
-CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B = 1, 2, 3, 4, 5
+# one large matrix on its own: the Llama-3-8B LM head (vocabulary x hidden)
+LLAMA3_8B_LM_HEAD = (("lm_head", 128256, 4096),)
+
+CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B, CONFIG_LM_HEAD = 1, 2, 3, 4, 5, 6
 
 
 def _workers() -> int:

@@ -99,3 +99,28 @@ def test_llama31_405b_block_t3(torch_dev, orc):
     ranges += [(int(b), int(b) + 2) for b in rng.integers(0, nt - 2, 5)]
     say("405B block: oracle ranges")
     check_sampled_ranges(torch, orc, c, out, ranges)
+
+
+def test_llama3_8b_lm_head(torch_dev, orc):
+    """One large matrix on its own (the Llama-3-8B LM head, 128256 x 4096 =
+    525,336,576 BF16 weights), one codebook, one launch."""
+    torch, dev = torch_dev
+    src, _ = synth.bf16_block(0, config=synth.CONFIG_LM_HEAD, shapes=synth.LLAMA3_8B_LM_HEAD)
+    assert src.size == 128256 * 4096
+    c = dfh.compress(0, src)
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dfh.df_decompress_checked(dc, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ok = True
+    step = 1 << 27
+    for lo in range(0, src.size, step):
+        hi = min(src.size, lo + step)
+        ref = torch.from_numpy(src[lo:hi].view(np.int16)).to(dev)
+        ok = ok and bool(torch.equal(out[lo:hi].view(torch.int16), ref))
+    assert ok
+    nt = int(c.info()["n_tiles"])
+    check_sampled_ranges(torch, orc, c, out, [(0, 8), (nt // 2, nt // 2 + 8), (nt - 8, nt)])
+    say("lm head ok", nt, "tiles")
