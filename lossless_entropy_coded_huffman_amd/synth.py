@@ -46,7 +46,8 @@ LLAMA31_405B_BLOCK = (
 # one large matrix on its own: the Llama-3-8B LM head (vocabulary x hidden)
 LLAMA3_8B_LM_HEAD = (("lm_head", 128256, 4096),)
 
-CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B, CONFIG_LM_HEAD = 1, 2, 3, 4, 5, 6
+CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B, CONFIG_LM_HEAD, CONFIG_FORWARD = \
+    1, 2, 3, 4, 5, 6, 7
 
 
 def _workers() -> int:

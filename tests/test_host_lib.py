@@ -200,3 +200,9 @@ def test_one_symbol_and_empty(orc):
     assert orc.check_dtab(0, c.info()["lengths"], np.asarray(c.section("dtab"))) == 0
     e = dfh.compress(1, np.zeros(0, np.uint8))
     assert e.info()["n_tiles"] == 0 and list(np.asarray(e.section("tile_out"))) == [0]
+
+
+def test_forward_block_shape_matches_benchmark_block():
+    from lossless_entropy_coded_huffman_amd import forward as fw, synth
+    assert fw.LLAMA3_8B.matrices() == synth.LLAMA3_8B_BLOCK
+    assert fw.LLAMA3_8B.elements() == synth.block_elems(synth.LLAMA3_8B_BLOCK) == 218_103_808
