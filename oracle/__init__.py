@@ -15,8 +15,10 @@ What it computes (sources by page title and section heading):
   ("Kernel de GPU em 2 etapas e metadados auxiliares"); hierarchical 256-entry
   tables ("Decodificacao com LUT hierarquica").
 * EntroLLM ("EntroLLM: Entropy Encoded Weight Compression...", section
-  "Metodologia"): Huffman coding of whole uint8 codes, decoded in parallel on
-  CPU threads.
+  "Metodologia"): Huffman coding of whole uint8 codes, and of uint4 codes as a
+  16-symbol alphabet (packed two per byte, element 2j in the low nibble of
+  byte j), decoded in parallel on CPU threads.  For uint4 the decoders return
+  one symbol byte per element; ``pack_u4`` packs them.
 
 Every function here has pins in ``tests/test_oracle_*.py`` that do not rely on
 the oracle itself (brute force, closed forms, invariants, round trips).
@@ -32,6 +34,7 @@ import numpy as np
 
 KIND_BF16 = 0
 KIND_U8 = 1
+KIND_U4 = 2
 MAX_LEN = 32
 DTAB_BITS = 12
 
@@ -86,6 +89,7 @@ def _load():
             "oracle_decode_tiles": (I, [I, P, P, U64, P, P, U64, U64, P, P, I]),
             "oracle_check_dtab": (ctypes.c_int64, [I, P, P, I]),
             "oracle_decode_tile_range": (I, [I, P, P, U64, P, P, U64, U64, U64, P, P]),
+            "oracle_pack_u4": (I, [P, U64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -124,10 +128,29 @@ def merge_bf16(e, sm) -> np.ndarray:
     return out
 
 
-def histogram(kind: int, src) -> np.ndarray:
+def _count(kind: int, a: np.ndarray, n: int | None) -> int:
+    """Elements in src: its size, or for uint4 (packed bytes) n, default 2 per byte."""
+    if kind != KIND_U4:
+        return a.size
+    n = 2 * a.size if n is None else int(n)
+    if (n + 1) // 2 > a.size:
+        raise ValueError("uint4 input shorter than n elements")
+    return n
+
+
+def pack_u4(syms) -> np.ndarray:
+    """Symbols 0..15, one per byte -> packed bytes (element 2j in the low nibble)."""
+    a = np.ascontiguousarray(syms, np.uint8).reshape(-1)
+    out = np.zeros((a.size + 1) // 2, np.uint8)
+    if _load().oracle_pack_u4(_ptr(a), a.size, _ptr(out)) != 0:
+        raise ValueError("symbol above 15")
+    return out
+
+
+def histogram(kind: int, src, n: int | None = None) -> np.ndarray:
     a = _src(kind, src)
     h = np.zeros(256, np.uint64)
-    if _load().oracle_histogram(kind, _ptr(a), a.size, _ptr(h)) != 0:
+    if _load().oracle_histogram(kind, _ptr(a), _count(kind, a, n), _ptr(h)) != 0:
         raise ValueError("bad kind")
     return h
 
@@ -166,21 +189,22 @@ def canonical_codes(lengths) -> np.ndarray:
     return out
 
 
-def encode(kind: int, src, lengths) -> dict:
+def encode(kind: int, src, lengths, n: int | None = None) -> dict:
     """Encode with the given lengths.  Returns a dict with the scalars
     n, total_bits, n_threads, n_tiles, max_tile_elems and the sections
-    bitstream, gaps, tile_out, sign_mantissa (None for uint8)."""
+    bitstream, gaps, tile_out, sign_mantissa (None unless BF16)."""
     lib = _load()
     a = _src(kind, src)
+    n = _count(kind, a, n)
     ln = np.ascontiguousarray(lengths, np.uint8)
     lay = _Layout()
-    if lib.oracle_layout(kind, _ptr(a), a.size, _ptr(ln), ctypes.byref(lay)) != 0:
+    if lib.oracle_layout(kind, _ptr(a), n, _ptr(ln), ctypes.byref(lay)) != 0:
         raise ValueError("a symbol of the input has no code")
     bs = np.zeros(lay.bitstream_bytes, np.uint8)
     gaps = np.zeros(lay.gaps_bytes, np.uint8)
     tile_out = np.zeros(lay.tile_out_entries, np.uint64)
     sm = np.zeros(lay.sm_bytes, np.uint8) if kind == KIND_BF16 else None
-    rc = lib.oracle_encode(kind, _ptr(a), a.size, _ptr(ln), ctypes.byref(lay), _ptr(bs),
+    rc = lib.oracle_encode(kind, _ptr(a), n, _ptr(ln), ctypes.byref(lay), _ptr(bs),
                            _ptr(gaps), _ptr(tile_out), _ptr(sm))
     if rc != 0:
         raise RuntimeError("oracle_encode failed: %d" % rc)
@@ -198,11 +222,11 @@ def build_lut(lengths, cap: int = 64) -> tuple[np.ndarray, int]:
     return lut[: n.value * 256].copy(), n.value
 
 
-def compress(kind: int, src, max_len: int = MAX_LEN) -> dict:
+def compress(kind: int, src, max_len: int = MAX_LEN, n: int | None = None) -> dict:
     """histogram -> lengths -> encode -> hierarchical tables, all by the oracle."""
-    h = histogram(kind, src)
+    h = histogram(kind, src, n)
     ln = code_lengths(h, max_len)
-    c = encode(kind, src, ln)
+    c = encode(kind, src, ln, n)
     c["lut"], c["n_luts"] = build_lut(ln)
     c["hist"] = h
     return c
@@ -213,7 +237,7 @@ def decode_serial(kind: int, lengths, bitstream, n: int, sign_mantissa=None) -> 
     ln = np.ascontiguousarray(lengths, np.uint8)
     bs = np.ascontiguousarray(bitstream, np.uint8)
     out = np.empty(n, np.uint16 if kind == KIND_BF16 else np.uint8)
-    sm = None if kind == KIND_U8 else np.ascontiguousarray(sign_mantissa, np.uint8)
+    sm = None if kind != KIND_BF16 else np.ascontiguousarray(sign_mantissa, np.uint8)
     if kind == KIND_BF16 and (sm is None or sm.size < n):
         raise ValueError("sign_mantissa too short")
     if _load().oracle_decode_serial(kind, _ptr(ln), _ptr(bs), bs.size, n, _ptr(sm), _ptr(out)) != 0:
@@ -232,7 +256,7 @@ def decode_tiles(c: dict, cpu_threads: int = 1, out: np.ndarray | None = None) -
     bs = np.ascontiguousarray(c["bitstream"], np.uint8)
     gaps = np.ascontiguousarray(c["gaps"], np.uint8)
     to = np.ascontiguousarray(c["tile_out"], np.uint64)
-    sm = None if kind == KIND_U8 else np.ascontiguousarray(c["sign_mantissa"], np.uint8)
+    sm = None if kind != KIND_BF16 else np.ascontiguousarray(c["sign_mantissa"], np.uint8)
     rc = _load().oracle_decode_tiles(kind, _ptr(ln), _ptr(bs), bs.size, _ptr(gaps), _ptr(to),
                                      int(c["n_tiles"]), int(c["n_threads"]), _ptr(sm), _ptr(out),
                                      int(cpu_threads))
@@ -252,7 +276,7 @@ def decode_tile_range(c: dict, b0: int, b1: int) -> np.ndarray:
     ln = np.ascontiguousarray(c["lengths"], np.uint8)
     bs = np.ascontiguousarray(c["bitstream"], np.uint8)
     gaps = np.ascontiguousarray(c["gaps"], np.uint8)
-    sm = None if kind == KIND_U8 else np.ascontiguousarray(c["sign_mantissa"], np.uint8)
+    sm = None if kind != KIND_BF16 else np.ascontiguousarray(c["sign_mantissa"], np.uint8)
     # dst points lo elements before the buffer so that element i lands at i - lo;
     # the worker writes only indices in [lo, hi)
     esz = out.itemsize

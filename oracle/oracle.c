@@ -4,7 +4,8 @@
  * A plain, slow, scalar CPU oracle for lossless Huffman coding of LLM weights:
  *   - the DFloat11 scheme (BF16 exponent byte Huffman-coded, sign and mantissa
  *     kept raw), and
- *   - the EntroLLM scheme (whole uint8 quantised codes Huffman-coded).
+ *   - the EntroLLM scheme (whole uint8 quantised codes Huffman-coded, and
+ *     uint4 codes as a 16-symbol alphabet).
  *
  * Only the test suite, the smoke check and the CPU-baseline leg of the
  * benchmark may load this library.  It shares no code, header, table or
@@ -38,7 +39,10 @@
  *   - gap of chunk t = (first code start >= 64 t) - 64 t, packed in 5-bit
  *     fields, least significant bit first;
  *   - tile_out[b] = number of codes that start before bit 16384 b, with one
- *     extra final entry equal to n.
+ *     extra final entry equal to n;
+ *   - uint4 codes are packed two per byte, element 2j in the low nibble of
+ *     byte j (a final odd element leaves the high nibble zero), both in the
+ *     input and in the decoded output.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -47,6 +51,7 @@
 
 #define O_KIND_BF16 0
 #define O_KIND_U8 1
+#define O_KIND_U4 2
 #define O_MAX_LEN 32
 #define O_CHUNK_BITS 64             /* 8 bytes of stream per thread            */
 #define O_THREADS_PER_TILE 256
@@ -84,19 +89,36 @@ int oracle_merge_bf16(const uint8_t *expo, const uint8_t *sm, uint64_t n,
 }
 
 /* The coded symbol of element i: the exponent byte for BF16, the byte itself
- * for uint8 ([ENTRO, "Metodologia"], Huffman coding of the quantised codes). */
+ * for uint8, the nibble for uint4 ([ENTRO, "Metodologia"], Huffman coding of
+ * the quantised codes, 8-bit or 4-bit). */
 static uint8_t symbol_of(int kind, const void *src, uint64_t i) {
   if (kind == O_KIND_BF16) {
     uint16_t u = ((const uint16_t *)src)[i];
     return (uint8_t)((u >> 7) & 0xFF);
   }
+  if (kind == O_KIND_U4) {
+    uint8_t b = ((const uint8_t *)src)[i / 2];
+    return (uint8_t)((i % 2 == 0) ? (b & 0x0F) : (b >> 4));
+  }
   return ((const uint8_t *)src)[i];
+}
+
+/* uint4 output: pack n symbols (one per byte, values 0..15) two per byte,
+ * element 2j in the low nibble of byte j; writes (n + 1) / 2 bytes. */
+int oracle_pack_u4(const uint8_t *syms, uint64_t n, uint8_t *out) {
+  for (uint64_t j = 0; j < (n + 1) / 2; j++) {
+    uint8_t lo = syms[2 * j];
+    uint8_t hi = (2 * j + 1 < n) ? syms[2 * j + 1] : 0;
+    if (lo > 15 || hi > 15) return -1;
+    out[j] = (uint8_t)(lo | (hi << 4));
+  }
+  return 0;
 }
 
 /* Histogram of the coded symbol.  [DF11, "O formato DFloat11"]: the tree is
  * built from the distribution of the exponent values.                       */
 int oracle_histogram(int kind, const void *src, uint64_t n, uint64_t *hist) {
-  if (kind != O_KIND_BF16 && kind != O_KIND_U8) return -1;
+  if (kind != O_KIND_BF16 && kind != O_KIND_U8 && kind != O_KIND_U4) return -1;
   for (int s = 0; s < 256; s++) hist[s] = 0;
   for (uint64_t i = 0; i < n; i++) hist[symbol_of(kind, src, i)]++;
   return 0;
@@ -552,6 +574,10 @@ static int decode_one(const canon_t *c, const uint8_t *stream, uint64_t *pos,
   return -1;
 }
 
+/* Output element i.  BF16: the weight from exponent and sign|mantissa.
+ * uint8 and uint4: the symbol, one byte per element (oracle_pack_u4 packs
+ * the uint4 result; writing single bytes keeps the tile-range workers of
+ * different threads off each other's bytes). */
 static void emit(int kind, void *dst, uint64_t i, uint8_t sym, const uint8_t *sm) {
   if (kind == O_KIND_BF16) {
     uint16_t sign = (uint16_t)(sm[i] >> 7), mant = (uint16_t)(sm[i] & 0x7F);

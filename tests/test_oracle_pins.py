@@ -479,3 +479,46 @@ def test_tile_range_decode_matches_whole(orc):
         part = orc.decode_tile_range(c, b0, b1)
         lo, hi = int(c["tile_out"][b0]), int(c["tile_out"][b1])
         assert np.array_equal(part, src[lo:hi])
+
+
+# ------------------------------------------------------------- uint4 (EntroLLM)
+def np_pack_u4(s):
+    """Independent packing: element 2j in the low nibble of byte j."""
+    s = np.asarray(s, np.uint8)
+    if s.size % 2:
+        s = np.concatenate([s, np.zeros(1, np.uint8)])
+    return (s[0::2] | (s[1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 17, 1000, 1001])
+def test_u4_pack_and_histogram(orc, n):
+    rng = np.random.default_rng(n)
+    s = rng.integers(0, 16, n).astype(np.uint8)
+    packed = orc.pack_u4(s)
+    assert np.array_equal(packed, np_pack_u4(s))
+    h = orc.histogram(orc.KIND_U4, packed, n)
+    assert np.array_equal(h[:16], np.bincount(s, minlength=16)) and h[16:].sum() == 0
+    with pytest.raises(ValueError):
+        orc.pack_u4(np.array([16], np.uint8))
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 255, 16383, 16384, 16385, 60001, 150_000])
+def test_u4_sections_equal_u8_of_the_same_symbols(orc, n):
+    # the uint4 kind differs from uint8 only in where a symbol is read from, so
+    # with the same lengths every section must be the same as for the unpacked
+    # symbols coded as uint8
+    rng = np.random.default_rng(100 + n)
+    q = np.clip(np.rint(rng.normal(7.5, 2.2, n)), 0, 15).astype(np.uint8)
+    packed = np_pack_u4(q)
+    if n % 2:
+        packed[-1] |= 0xA0          # the unused high nibble must be ignored
+    c4 = orc.compress(orc.KIND_U4, packed, n=n)
+    c8 = orc.encode(orc.KIND_U8, q, c4["lengths"])
+    for k in ("bitstream", "gaps", "tile_out"):
+        assert np.array_equal(c4[k], c8[k]), k
+    assert (c4["n"], c4["total_bits"], c4["n_tiles"]) == (c8["n"], c8["total_bits"], c8["n_tiles"])
+    assert max(c4["lengths"]) <= 15          # 16 symbols: depth at most 15
+    d = orc.decode_tiles(c4, 4)
+    assert np.array_equal(d, q)
+    assert np.array_equal(orc.decode_serial(orc.KIND_U4, c4["lengths"], c4["bitstream"], n), q)
+    assert np.array_equal(orc.pack_u4(d), np_pack_u4(q))
