@@ -10,8 +10,11 @@
  * before each transformer block runs.  The EntroLLM summary ("EntroLLM:
  * Entropy Encoded Weight Compression for Efficient Large Language Model
  * Inference on Edge Devices", section "Metodologia") Huffman codes whole
- * uint8 quantised weights and decodes them in parallel.  This library covers
- * both: DF_KIND_BF16 codes the exponent byte, DF_KIND_U8 codes the byte.
+ * uint8 quantised weights and decodes them in parallel, and names 4-bit
+ * codes as well.  This library covers all three: DF_KIND_BF16 codes the
+ * exponent byte, DF_KIND_U8 codes the byte, DF_KIND_U4 codes the nibble
+ * (16-symbol alphabet; elements packed two per byte, element 2j in the low
+ * nibble of byte j, in the input and in the decoded output).
  *
  * Host calls build a codebook and encode into a library-owned container;
  * device calls decompress a container whose sections the caller has copied
@@ -26,7 +29,7 @@
  *     synchronising, allocating, or copying between host and device.
  *
  * Container format (little-endian).  Element i has symbol e_i (the BF16
- * exponent byte (u >> 7) & 0xFF, or the uint8 value).  Codes are canonical
+ * exponent byte (u >> 7) & 0xFF, the uint8 value, or the uint4 nibble).  Codes are canonical
  * (RFC 1951 section 3.2.2) from lengths[256] (0 = unused, 1..32).  Sections:
  *   BITSTREAM      codes of e_0, e_1, ... concatenated, packed least
  *                  significant bit first inside each byte, each code emitted
@@ -44,7 +47,8 @@
  *                  block b); the last entry is n.  (Same section: one output
  *                  position per thread block.)
  *   SIGN_MANTISSA  BF16 only: byte i = (sign << 7) | mantissa7 of element i;
- *                  round_up(n, 64) bytes, zero padded; 0 bytes for uint8.
+ *                  round_up(n, 64) bytes, zero padded; 0 bytes for uint8
+ *                  and uint4.
  *                  (Digest, "O formato DFloat11": PackedSignMantissa.)
  *   LUT            uint16[n_luts * 256]: the code tree cut into height-8
  *                  subtrees, one 256-entry table each, indexed by the next 8
@@ -84,7 +88,7 @@ typedef enum {
   DF_ERR_IO = -7        /* file could not be read or written */
 } df_status;
 
-typedef enum { DF_KIND_BF16 = 0, DF_KIND_U8 = 1 } df_kind;
+typedef enum { DF_KIND_BF16 = 0, DF_KIND_U8 = 1, DF_KIND_U4 = 2 } df_kind;
 
 typedef enum {
   DF_SEC_BITSTREAM = 0,
@@ -127,8 +131,9 @@ typedef struct df_container df_container; /* opaque, library-owned */
 
 /* Histogram of the coded symbol (digest, "O formato DFloat11": the tree
  * follows the distribution of exponent values).  src holds n uint16 BF16
- * bit patterns (DF_KIND_BF16) or n bytes (DF_KIND_U8); hist receives 256
- * counts.  Multi-threaded on the host.  DF_ERR_ARG on a null pointer (src
+ * bit patterns (DF_KIND_BF16), n bytes (DF_KIND_U8) or (n + 1) / 2 bytes of
+ * packed nibbles (DF_KIND_U4; a final odd element's high nibble is
+ * ignored); hist receives 256 counts.  Multi-threaded on the host.  DF_ERR_ARG on a null pointer (src
  * may be null when n == 0) or a bad kind. */
 df_status df_histogram(df_kind kind, const void *src, uint64_t n, uint64_t hist[256]);
 
@@ -176,8 +181,8 @@ const char *df_status_string(df_status s);
 /* ------------------------------------------------------------------ device */
 
 /* Borrowed device pointers to a container's sections (caller-owned, e.g.
- * torch tensors) plus its header scalars.  sign_mantissa is NULL for
- * DF_KIND_U8.  Every section must have the size df_info reports. */
+ * torch tensors) plus its header scalars.  sign_mantissa is NULL unless the
+ * kind is DF_KIND_BF16.  Every section must have the size df_info reports. */
 typedef struct {
   df_kind kind;
   uint32_t n_luts;
@@ -195,8 +200,9 @@ typedef struct {
   const uint64_t *dtab;
 } df_device_view;
 
-/* Decompress one container into dst (n * 2 bytes of BF16 bit patterns, or
- * n bytes of uint8; 16-byte aligned, not aliasing any section).  The
+/* Decompress one container into dst (n * 2 bytes of BF16 bit patterns, n
+ * bytes of uint8, or (n + 1) / 2 bytes of packed uint4 with a final odd
+ * element's high nibble zero; 16-byte aligned, not aliasing any section).  The
  * digest's "Kernel de GPU em 2 etapas e metadados auxiliares": each thread
  * owns 8 stream bytes and decodes the codes that start in them, first only
  * counting, then (after a prefix sum of the counts over the thread block)

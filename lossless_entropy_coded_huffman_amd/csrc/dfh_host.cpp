@@ -64,8 +64,15 @@ void parallel_ranges(uint64_t n, unsigned parts, F f) {
   for (auto &t : pool) t.join();
 }
 
+inline bool valid_kind(int kind) {
+  return kind == DF_KIND_BF16 || kind == DF_KIND_U8 || kind == DF_KIND_U4;
+}
+
+// The coded symbol of element i: BF16 exponent byte, uint8 byte, or uint4
+// nibble (element 2j in the low nibble of byte j).
 inline uint8_t sym_at(df_kind kind, const void *src, uint64_t i) {
   if (kind == DF_KIND_BF16) return (uint8_t)((((const uint16_t *)src)[i] >> 7) & 0xFF);
+  if (kind == DF_KIND_U4) return (uint8_t)((((const uint8_t *)src)[i >> 1] >> (4 * (i & 1))) & 0xF);
   return ((const uint8_t *)src)[i];
 }
 
@@ -353,7 +360,7 @@ const char *df_status_string(df_status s) {
 }
 
 df_status df_histogram(df_kind kind, const void *src, uint64_t n, uint64_t hist[256]) {
-  if (!hist || (n && !src) || (kind != DF_KIND_BF16 && kind != DF_KIND_U8)) return DF_ERR_ARG;
+  if (!hist || (n && !src) || !valid_kind(kind)) return DF_ERR_ARG;
   unsigned parts = n < (1u << 20) ? 1 : host_threads();
   std::vector<uint64_t> local((size_t)parts * 256, 0);
   parallel_ranges(n, parts, [&](unsigned k, uint64_t b, uint64_t e) {
@@ -387,7 +394,7 @@ df_status df_build_codebook(const uint64_t hist[256], uint32_t max_len, uint8_t 
 
 df_status df_encode(df_kind kind, const void *src, uint64_t n, const uint8_t lengths[256],
                     df_container **out) {
-  if (!out || !lengths || (n && !src) || (kind != DF_KIND_BF16 && kind != DF_KIND_U8))
+  if (!out || !lengths || (n && !src) || !valid_kind(kind))
     return DF_ERR_ARG;
   *out = nullptr;
   uint64_t kr = kraft_scaled(lengths);
@@ -521,7 +528,7 @@ void df_container_free(df_container *c) { delete c; }
 df_status df_container_validate(const df_container *c) {
   if (!c) return DF_ERR_ARG;
   const df_info &in = c->info;
-  if (in.kind != DF_KIND_BF16 && in.kind != DF_KIND_U8) return DF_ERR_FORMAT;
+  if (!valid_kind(in.kind)) return DF_ERR_FORMAT;
   if (in.bytes_per_thread != DF_BYTES_PER_THREAD || in.threads_per_tile != DF_THREADS_PER_TILE ||
       in.max_len != DF_MAX_LEN)
     return DF_ERR_FORMAT;
@@ -610,7 +617,7 @@ df_status df_container_load(const char *path, df_container **out) {
   df_status st = DF_OK;
   if (!c) st = DF_ERR_ALLOC;
   else if (fread(&h, sizeof h, 1, f) != 1 || fread(c->info.lengths, 256, 1, f) != 1) st = DF_ERR_FORMAT;
-  else if (h.magic != kMagic || h.version != kVersion || h.kind > 1 || h.n_luts > DF_MAX_LUTS)
+  else if (h.magic != kMagic || h.version != kVersion || h.kind > 2 || h.n_luts > DF_MAX_LUTS)
     st = DF_ERR_FORMAT;
   if (st == DF_OK) {
     df_info &in = c->info;

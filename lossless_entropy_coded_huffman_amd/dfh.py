@@ -17,6 +17,7 @@ import torch  # noqa: F401  (loads the HIP runtime libdfh binds to)
 
 KIND_BF16 = 0
 KIND_U8 = 1
+KIND_U4 = 2   # two elements per byte, element 2j in the low nibble of byte j
 SEC_BITSTREAM, SEC_GAPS, SEC_TILE_OUT, SEC_SIGN_MANTISSA, SEC_LUT, SEC_DTAB = range(6)
 SECTION_NAMES = ("bitstream", "gaps", "tile_out", "sign_mantissa", "lut", "dtab")
 MAX_LEN = 32
@@ -116,11 +117,29 @@ def _host_array(kind: int, src) -> np.ndarray:
     return a
 
 
+def _elements(kind: int, a: np.ndarray, n) -> int:
+    """Element count of a host array: its size, or for uint4 (packed bytes) n,
+    by default two per byte."""
+    if kind != KIND_U4:
+        if n is not None and int(n) != a.size:
+            raise ValueError("n is only given for uint4 input")
+        return a.size
+    n = 2 * a.size if n is None else int(n)
+    if n < 0 or (n + 1) // 2 > a.size:
+        raise ValueError("uint4 input holds fewer than n elements")
+    return n
+
+
+def output_bytes(kind: int, n: int) -> int:
+    """Bytes of a decoded container of n elements."""
+    return 2 * n if kind == KIND_BF16 else n if kind == KIND_U8 else (n + 1) // 2
+
+
 # ------------------------------------------------------------------- host API
-def df_histogram(kind: int, src) -> np.ndarray:
+def df_histogram(kind: int, src, n=None) -> np.ndarray:
     a = _host_array(kind, src)
     h = np.zeros(256, np.uint64)
-    _check(lib().df_histogram(kind, a.ctypes.data, a.size, h.ctypes.data), "df_histogram")
+    _check(lib().df_histogram(kind, a.ctypes.data, _elements(kind, a, n), h.ctypes.data), "df_histogram")
     return h
 
 
@@ -167,12 +186,12 @@ class Container:
             pass
 
 
-def df_encode(kind: int, src, lengths) -> Container:
+def df_encode(kind: int, src, lengths, n=None) -> Container:
     a = _host_array(kind, src)
     ln = np.ascontiguousarray(lengths, np.uint8)
     out = ctypes.c_void_p()
-    _check(lib().df_encode(kind, a.ctypes.data if a.size else None, a.size, ln.ctypes.data,
-                           ctypes.byref(out)), "df_encode")
+    _check(lib().df_encode(kind, a.ctypes.data if a.size else None, _elements(kind, a, n),
+                           ln.ctypes.data, ctypes.byref(out)), "df_encode")
     return Container(out.value)
 
 
@@ -236,10 +255,11 @@ def df_container_free(c: Container):
     c.free()
 
 
-def compress(kind: int, src, max_len: int = MAX_LEN) -> Container:
-    """df_histogram -> df_build_codebook -> df_encode."""
+def compress(kind: int, src, max_len: int = MAX_LEN, n=None) -> Container:
+    """df_histogram -> df_build_codebook -> df_encode.  For uint4, src is the
+    packed bytes and n the element count (default: two per byte)."""
     a = _host_array(kind, src)
-    return df_encode(kind, a, df_build_codebook(df_histogram(kind, a), max_len))
+    return df_encode(kind, a, df_build_codebook(df_histogram(kind, a, n), max_len), n)
 
 
 # ----------------------------------------------------------------- device API
@@ -281,8 +301,9 @@ class DeviceContainer:
         return sum(v for k, v in self.info["section_bytes"].items() if k != "dtab")
 
     def empty_output(self) -> torch.Tensor:
-        dt = torch.bfloat16 if self.kind == KIND_BF16 else torch.uint8
-        return torch.empty(self.n, dtype=dt, device=self.device)
+        if self.kind == KIND_BF16:
+            return torch.empty(self.n, dtype=torch.bfloat16, device=self.device)
+        return torch.empty(output_bytes(self.kind, self.n), dtype=torch.uint8, device=self.device)
 
 
 def to_device(c: Container, device="cuda") -> DeviceContainer:
@@ -298,7 +319,7 @@ def _stream_handle(stream, device):
 
 
 def _check_dst(dc: DeviceContainer, dst: torch.Tensor):
-    need = dc.n * (2 if dc.kind == KIND_BF16 else 1)
+    need = output_bytes(dc.kind, dc.n)
     if not dst.is_cuda or not dst.is_contiguous() or dst.numel() * dst.element_size() < need:
         raise ValueError("dst must be a contiguous device tensor of at least %d bytes" % need)
 

@@ -46,8 +46,8 @@ LLAMA31_405B_BLOCK = (
 # one large matrix on its own: the Llama-3-8B LM head (vocabulary x hidden)
 LLAMA3_8B_LM_HEAD = (("lm_head", 128256, 4096),)
 
-CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B, CONFIG_LM_HEAD, CONFIG_FORWARD = \
-    1, 2, 3, 4, 5, 6, 7
+CONFIG_C1, CONFIG_8B_BF16, CONFIG_8B_U8, CONFIG_8B_FULL, CONFIG_405B, CONFIG_LM_HEAD, CONFIG_FORWARD, \
+    CONFIG_8B_U4 = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _workers() -> int:
@@ -157,6 +157,59 @@ def u8_block(seed: int = 0, config: int = CONFIG_8B_U8, block: int = 0, shapes=L
         x = np.empty(r * c, np.float32)
         _fill(x, (seed, config, block, m), "normal", s, False)
         layers.append((name, quantize_u8(x, bool(asym)), bool(asym)))
+    return layers
+
+
+def quantize_u4(x: np.ndarray, asymmetric: bool) -> np.ndarray:
+    """Per-tensor uint4 quantisation of one layer, the 4-bit counterpart of
+    quantize_u8 (same reading, 16 levels), one value 0..15 per byte:
+      unsigned:   s = max|x| / 7,            q = clamp(rint(x / s) + 8, 0, 15)
+      asymmetric: s = (max - min) / 15,      zp = clamp(rint(-min / s), 0, 15),
+                  q = clamp(rint(x / s) + zp, 0, 15)"""
+    x = np.asarray(x, np.float32)
+    if x.size == 0:
+        return np.zeros(0, np.uint8)
+    if asymmetric:
+        lo, hi = np.float32(x.min()), np.float32(x.max())
+        s = np.float32((hi - lo) / np.float32(15))
+        s = s if s > 0 else np.float32(1)
+        zp = np.clip(np.rint(-lo / s), 0, 15)
+        q = np.rint(x / s) + zp
+    else:
+        s = np.float32(np.abs(x).max() / np.float32(7))
+        s = s if s > 0 else np.float32(1)
+        q = np.rint(x / s) + np.float32(8)
+    return np.clip(q, 0, 15).astype(np.uint8)
+
+
+def pack_u4(q: np.ndarray) -> np.ndarray:
+    """Values 0..15 -> packed bytes, element 2j in the low nibble of byte j
+    (input layout of the uint4 kind)."""
+    q = np.asarray(q, np.uint8).reshape(-1)
+    if q.size % 2:
+        q = np.concatenate([q, np.zeros(1, np.uint8)])
+    return (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_u4(packed: np.ndarray, n: int) -> np.ndarray:
+    """Packed bytes -> n values 0..15."""
+    b = np.asarray(packed, np.uint8).reshape(-1)
+    out = np.empty(2 * b.size, np.uint8)
+    out[0::2] = b & 0x0F
+    out[1::2] = b >> 4
+    return out[:n]
+
+
+def u4_block(seed: int = 0, config: int = CONFIG_8B_U4, block: int = 0, shapes=LLAMA3_8B_BLOCK):
+    """The EntroLLM-style 4-bit block: as u8_block, quantised to uint4 and
+    packed two per byte.  Returns [(name, packed uint8 array, n, asymmetric), ...]."""
+    g = _gen(seed, config, block)
+    params = [(int(g.integers(0, 2)), float(g.uniform(0.01, 0.04))) for _ in shapes]
+    layers = []
+    for m, ((name, r, c), (asym, s)) in enumerate(zip(shapes, params)):
+        x = np.empty(r * c, np.float32)
+        _fill(x, (seed, config, block, m), "normal", s, False)
+        layers.append((name, pack_u4(quantize_u4(x, bool(asym))), r * c, bool(asym)))
     return layers
 
 

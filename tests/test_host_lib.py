@@ -31,11 +31,21 @@ def test_library_exports_every_declared_symbol():
 
 
 def inputs(kind, n, seed, dist="normal"):
+    """Host input of n elements; for uint4 the packed bytes."""
     rng = np.random.default_rng(seed)
     if kind == dfh.KIND_BF16:
         x = rng.standard_t(3, n) * 0.02 if dist == "t3" else rng.normal(0, 0.02, n)
         return synth.bf16_rne(x.astype(np.float32))
-    return synth.quantize_u8(rng.normal(0, 0.02, n).astype(np.float32), bool(seed & 1))
+    x = rng.normal(0, 0.02, n).astype(np.float32)
+    if kind == dfh.KIND_U4:
+        return synth.pack_u4(synth.quantize_u4(x, bool(seed & 1)))
+    return synth.quantize_u8(x, bool(seed & 1))
+
+
+def decoded_of(kind, src, n):
+    """What the decoder must return for an input (oracle's view for uint4:
+    one symbol byte per element)."""
+    return synth.unpack_u4(src, n) if kind == dfh.KIND_U4 else src
 
 
 def lib_sections(c):
@@ -50,29 +60,30 @@ def as_oracle_container(c):
     return d
 
 
-@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("kind", [0, 1, 2])
 @pytest.mark.parametrize("n", EDGE_SIZES)
 def test_sections_identical_to_oracle(orc, kind, n):
     src = inputs(kind, n, n + kind)
-    h = dfh.df_histogram(kind, src)
-    assert np.array_equal(h, orc.histogram(kind, src))
+    nn = n if kind == dfh.KIND_U4 else None
+    h = dfh.df_histogram(kind, src, nn)
+    assert np.array_equal(h, orc.histogram(kind, src, nn))
     ln = dfh.df_build_codebook(h)
     assert np.array_equal(ln, orc.code_lengths(h))
-    c = dfh.df_encode(kind, src, ln)
-    o = orc.encode(kind, src, ln)
+    c = dfh.df_encode(kind, src, ln, nn)
+    o = orc.encode(kind, src, ln, nn)
     o["lut"], o["n_luts"] = orc.build_lut(ln)
     inf = c.info()
     for k in ("n", "total_bits", "n_threads", "n_tiles", "max_tile_elems", "n_luts"):
         assert inf[k] == o[k], k
     got = lib_sections(c)
     for k in SECTIONS:
-        if k == "sign_mantissa" and kind == 1:
+        if k == "sign_mantissa" and kind != 0:
             assert got[k].size == 0
             continue
         assert np.array_equal(got[k], o[k]), k
     assert orc.check_dtab(kind, ln, got["dtab"]) == 0
     c.validate()
-    assert np.array_equal(orc.decode_tiles(as_oracle_container(c), 4), src)
+    assert np.array_equal(orc.decode_tiles(as_oracle_container(c), 4), decoded_of(kind, src, n))
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -142,15 +153,28 @@ def test_heavy_tail_reaches_long_codes(orc):
         assert np.array_equal(np.asarray(c.section(k)), o[k]), k
 
 
-def test_save_load_round_trip(tmp_path):
-    src = inputs(0, 50_000, 9)
-    c = dfh.compress(0, src)
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_save_load_round_trip(tmp_path, kind):
+    src = inputs(kind, 50_001, 9)
+    c = dfh.compress(kind, src, n=50_001 if kind == dfh.KIND_U4 else None)
     p = str(tmp_path / "c.dfh")
     c.save(p)
     c2 = dfh.df_container_load(p)
     for k in dfh.SECTION_NAMES:
         assert np.array_equal(np.asarray(c.section(k)), np.asarray(c2.section(k))), k
     assert c.info()["total_bits"] == c2.info()["total_bits"]
+    assert c2.info()["kind"] == kind and c2.info()["n"] == 50_001
+
+
+def test_u4_element_count_checks():
+    p = inputs(dfh.KIND_U4, 10, 1)
+    assert p.size == 5
+    with pytest.raises(ValueError):
+        dfh.compress(dfh.KIND_U4, p, n=11)       # more elements than nibbles
+    with pytest.raises(ValueError):
+        dfh.compress(dfh.KIND_U8, p, n=6)        # uint8: n must be the array size
+    assert dfh.compress(dfh.KIND_U4, p).info()["n"] == 10
+    assert dfh.output_bytes(dfh.KIND_U4, 11) == 6
 
 
 def test_load_rejects_corrupt_files(tmp_path):
