@@ -144,6 +144,14 @@ __device__ __forceinline__ uint2 merge4(uint32_t e4, uint32_t s4) {
   return make_uint2((x0 & 0x7F7F7F7Fu) | (y0 & 0x80808080u), (x1 & 0x7F7F7F7Fu) | (y1 & 0x80808080u));
 }
 
+// Eight uint4 symbols, one per byte in two words (elements 0..3, 4..7), as
+// four packed bytes, element 2j in the low nibble of byte j: t = w | w >> 4
+// puts pair (2j, 2j + 1) in byte 2j of each word, a byte permute gathers
+// bytes 0 and 2 of both.
+__device__ __forceinline__ uint32_t pack8(uint32_t w0, uint32_t w1) {
+  return __builtin_amdgcn_perm(w1 | (w1 >> 4), w0 | (w0 >> 4), 0x06040200u);
+}
+
 // A lane's position in its stream words: b2:b1:b0 holds the stream from
 // the current code on (bit 0 of b0 = first bit of the next code).  Built
 // from the chunk's three words w2:w1:w0 and the bit g (< 32) at which the
@@ -222,11 +230,16 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
 // each lane clears the granules it has just read, and the bytes from the
 // last granule up to `dirty` (the next lane-group's lookahead slack) are
 // cleared here too.
+//
+// uint4 packs a granule of 32 staging bytes into 16 output bytes and owns
+// the bytes whose low-nibble element is its own, [ceil(lo / 2), ceil(hi / 2))
+// relative to a / 2; he is hi_r + 1 when the element after the tile exists
+// (its symbol then sits at staging position hi_r), else hi_r.
 template <int KIND>
 __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t a, uint32_t lo_r,
-                                           uint32_t hi_r, uint32_t ngroups, uint32_t dirty,
+                                           uint32_t hi_r, uint32_t he, uint32_t ngroups, uint32_t dirty,
                                            const uint2 (&smv)[kPrefetch], uint32_t lane) {
-  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : 16u;
+  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : KIND == DF_KIND_U8 ? 16u : 32u;
   for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
     *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
   if (KIND == DF_KIND_BF16) {
@@ -259,6 +272,29 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
       if (e0 >= lo_r && e0 + 8 <= hi_r) *(uint4 *)(dst_t + e0) = o;
       else store_partial(dst_t, e0, lo_r, hi_r, o);
     }
+  } else if (KIND == DF_KIND_U4) {
+    uint8_t *dst_t = (uint8_t *)jb.dst + a / 2;
+    lds_v4 *ex_t = lds<lds_v4>(buf);
+    const uint32_t blo = (lo_r + 1) / 2, bhi = (hi_r + 1) / 2;
+    // the last byte's high nibble when no element follows the tile
+    const uint32_t kill = (he == hi_r && (hi_r & 1)) ? bhi - 1 : 0xFFFFFFFFu;
+    for (uint32_t g = lane; g < ngroups; g += kTPB) {
+      const v4u x0 = ex_t[2 * g], x1 = ex_t[2 * g + 1];
+      ex_t[2 * g] = (v4u){0u, 0u, 0u, 0u};
+      ex_t[2 * g + 1] = (v4u){0u, 0u, 0u, 0u};
+      uint4 o = make_uint4(pack8(x0.x, x0.y), pack8(x0.z, x0.w), pack8(x1.x, x1.y), pack8(x1.z, x1.w));
+      const uint32_t b0 = 16 * g;
+      if (kill - b0 < 16) {
+        const uint32_t m = ~(0xF0u << (8 * ((kill - b0) & 3)));
+        const uint32_t wk = (kill - b0) >> 2;
+        o.x &= wk == 0 ? m : ~0u;
+        o.y &= wk == 1 ? m : ~0u;
+        o.z &= wk == 2 ? m : ~0u;
+        o.w &= wk == 3 ? m : ~0u;
+      }
+      if (b0 >= blo && b0 + 16 <= bhi) *(v4u *)(dst_t + b0) = (v4u){o.x, o.y, o.z, o.w};
+      else store_partial(dst_t, b0, blo, bhi, o);
+    }
   } else {
     uint8_t *dst_t = (uint8_t *)jb.dst + a;
     lds_v4 *ex_t = lds<lds_v4>(buf);
@@ -273,7 +309,7 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
 }
 
 struct ChunkRegs {
-  uint32_t w0, w1, w2, g0, g1;
+  uint32_t w0, w1, w2, w3, g0, g1;  // w3: uint4 only (next-tile code, below)
 };
 
 // The stream words and gap fields of one lane of a tile.  Addresses are a
@@ -281,6 +317,7 @@ struct ChunkRegs {
 // A tile past the last (a group with no next tile) reads the last tile
 // again: the loads are issued on every path, so each step puts the same
 // number of loads in flight, in the same order.  Needs n_tiles >= 1.
+template <int KIND>
 __device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, uint32_t lane) {
   if (tile >= jb.n_tiles) tile = jb.n_tiles - 1;
   ChunkRegs c;
@@ -288,7 +325,14 @@ __device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, ui
   const uint2 w01 = *(const uint2 *)(bits_t + 2 * lane);
   c.w0 = w01.x;
   c.w1 = w01.y;
-  c.w2 = bits_t[2 * lane + 2];
+  if (KIND == DF_KIND_U4) {  // 128 bits (the stream has 16 bytes of padding)
+    const uint2 w23 = *(const uint2 *)(bits_t + 2 * lane + 2);
+    c.w2 = w23.x;
+    c.w3 = w23.y;
+  } else {
+    c.w2 = bits_t[2 * lane + 2];
+    c.w3 = 0;
+  }
   const uint32_t *gaps_t = jb.gaps + tile * (5 * kTPB / 32);  // 1280 bits per tile
   c.g0 = gaps_t[(5 * lane) >> 5];
   c.g1 = gaps_t[((5 * lane) >> 5) + 1];
@@ -336,7 +380,7 @@ void decode_kernel(const Batch batch) {
 
   const uint64_t step = (uint64_t)jb.wg_count * groups;
   uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
-  ChunkRegs nxt = load_chunk(jb, base + grp, lane);
+  ChunkRegs nxt = load_chunk<KIND>(jb, base + grp, lane);
   // the next tile's first and last output index, one step ahead
   k_u64 *tout = (k_u64 *)jb.tile_out;
   uint64_t nlo = 0, nhi = 0;
@@ -357,7 +401,7 @@ void decode_kernel(const Batch batch) {
   // reads, so one buffer per group suffices.
   bool have_prev = false;
   uint64_t prev_a = 0;
-  uint32_t prev_lo = 0, prev_hi = 0, prev_ng = 0, prev_dirty = 0;
+  uint32_t prev_lo = 0, prev_hi = 0, prev_he = 0, prev_ng = 0, prev_dirty = 0;
 
   for (; base < jb.n_tiles; base += step) {
     const uint64_t tile = base + grp;  // wave-uniform
@@ -378,8 +422,9 @@ void decode_kernel(const Batch batch) {
     }
     const ChunkRegs cur = nxt;
     asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
+    if (KIND == DF_KIND_U4) asm volatile("" ::"v"(cur.w3));
     uint64_t lo = nlo, hi = nhi;
-    nxt = load_chunk(jb, tile + step, lane);
+    nxt = load_chunk<KIND>(jb, tile + step, lane);
     if (tile + step < jb.n_tiles) {
       nlo = tout[tile + step];
       nhi = tout[tile + step + 1];
@@ -388,9 +433,10 @@ void decode_kernel(const Batch batch) {
     if (lo > hi) lo = hi;
     if (hi - lo > jb.max_tile_elems) hi = lo + jb.max_tile_elems;
     // output range relative to the store-granule-aligned base a
-    const uint64_t a = KIND == DF_KIND_BF16 ? (lo & ~7ull) : (lo & ~15ull);
+    const uint64_t a = KIND == DF_KIND_BF16 ? (lo & ~7ull) : KIND == DF_KIND_U8 ? (lo & ~15ull) : (lo & ~31ull);
     const uint32_t lo_r = (uint32_t)(lo - a), hi_r = (uint32_t)(hi - a);
-    const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : 16u;  // elements per store granule
+    // elements per 16-byte store granule
+    const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : KIND == DF_KIND_U8 ? 16u : 32u;
     const uint32_t ngroups = active ? (hi_r + gsz - 1) / gsz : 0u;
 
     // chunk bounds: codes start in [gap, E) of this lane's 64 stream bits
@@ -413,6 +459,7 @@ void decode_kernel(const Batch batch) {
     // counted; the entry that crosses E gives back its codes that start at
     // or past E (they are the next lane's first codes).
     uint32_t cnt = 0;
+    int32_t rem_end = 0;  // E minus where the walk stopped (<= 0)
     {
       Stream t = stream_at(cur.w0, cur.w1, cur.w2, gap);
       int32_t rem = (int32_t)(E - gap);  // bits left before E
@@ -432,6 +479,7 @@ void decode_kernel(const Batch batch) {
         const uint32_t r = (uint32_t)(rem + (int32_t)(h & 31));
         cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
       }
+      rem_end = rem;
     }
 
     // store the previous tile.  Its sign|mantissa registers are taken here,
@@ -439,11 +487,13 @@ void decode_kernel(const Batch batch) {
     // in flight, and the store pass starts with no other load outstanding.
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    if (have_prev) store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_ng, prev_dirty, smv, lane);
+    if (have_prev)
+      store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
     have_prev = active;
     prev_a = a;
     prev_lo = lo_r;
     prev_hi = hi_r;
+    prev_he = hi_r + (hi < jb.n ? 1u : 0u);
     prev_ng = ngroups;
 
     // prefix sum of the counts over the tile's 256 lanes
@@ -474,7 +524,8 @@ void decode_kernel(const Batch batch) {
     {
       uint32_t q = buf + lo_r + off;
       uint32_t qend = q + cnt;
-      if (lo_r + off + cnt + kSlack > out_bytes) {
+      const bool fits = lo_r + off + cnt + kSlack <= out_bytes;
+      if (!fits) {
         qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
       }
@@ -488,6 +539,24 @@ void decode_kernel(const Batch batch) {
         __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         q += e.y >> 24;
+      }
+      // uint4: a tile that ends at an odd element shares its last output
+      // byte with the next tile, and writes that whole byte, so it needs the
+      // next tile's first symbol at staging position hi_r.  The lane with
+      // the tile's last code has it from its last lookup's lookahead (q
+      // moved past qend) or, when that lookup ended exactly on a code
+      // boundary, decodes it here: the code starts E - rem_end bits into
+      // the lane's 128 bits (it is the lane's walk end, at most 31 bits past
+      // the chunk, so its 32-bit window lies inside them).
+      if (KIND == DF_KIND_U4 && fits && cnt > 0 && off + cnt == s0 + s1 + s2 + s3 && (hi & 1) &&
+          hi < jb.n && q == qend) {
+        const uint32_t p = E - (uint32_t)rem_end;
+        const uint32_t win = p >= 64 ? __builtin_amdgcn_alignbit(cur.w3, cur.w2, p - 64)
+                           : p >= 32 ? __builtin_amdgcn_alignbit(cur.w2, cur.w1, p - 32)
+                                     : __builtin_amdgcn_alignbit(cur.w1, cur.w0, p);
+        const uint32_t c = long_code<CHECKED>(n_luts, win, batch.err);
+        __hip_atomic_fetch_or(lds<lds_u32>(q & ~3u), (c & 0xFFu) << ((q & 3) * 8), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     __syncthreads();
@@ -503,7 +572,7 @@ void decode_kernel(const Batch batch) {
     }
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_ng, prev_dirty, smv, lane);
+    store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
   }
 }
 
@@ -520,6 +589,7 @@ std::mutex g_mu;
 typedef void (*KernelFn)(const Batch);
 KernelFn kernel_for(df_kind kind, bool checked) {
   if (kind == DF_KIND_BF16) return checked ? decode_kernel<DF_KIND_BF16, true> : decode_kernel<DF_KIND_BF16, false>;
+  if (kind == DF_KIND_U4) return checked ? decode_kernel<DF_KIND_U4, true> : decode_kernel<DF_KIND_U4, false>;
   return checked ? decode_kernel<DF_KIND_U8, true> : decode_kernel<DF_KIND_U8, false>;
 }
 
@@ -534,7 +604,7 @@ df_status device_props(DeviceProps *out) {
       return DF_ERR_HIP;
     // allow dynamic LDS up to the device limit; where the runtime needs no
     // opt-in the call may fail, which is harmless, so its error is cleared
-    const df_kind kinds[2] = {DF_KIND_BF16, DF_KIND_U8};
+    const df_kind kinds[3] = {DF_KIND_BF16, DF_KIND_U8, DF_KIND_U4};
     for (df_kind k : kinds)
       for (int c = 0; c < 2; c++)
         if (hipFuncSetAttribute((const void *)kernel_for(k, c != 0),
@@ -549,7 +619,7 @@ df_status device_props(DeviceProps *out) {
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 df_status check_view(const df_device_view *v, const void *dst) {
-  if (!v || (v->kind != DF_KIND_BF16 && v->kind != DF_KIND_U8)) return DF_ERR_ARG;
+  if (!v || (v->kind != DF_KIND_BF16 && v->kind != DF_KIND_U8 && v->kind != DF_KIND_U4)) return DF_ERR_ARG;
   if (v->n == 0) return DF_OK;
   if (!dst || !aligned(dst, 16)) return DF_ERR_ARG;
   if (!v->bitstream || !v->gaps || !v->tile_out || !v->lut || !v->dtab) return DF_ERR_ARG;
@@ -567,7 +637,9 @@ df_status check_view(const df_device_view *v, const void *dst) {
   return DF_OK;
 }
 
-uint32_t out_bytes_for(uint32_t max_tile_elems) {
+uint32_t out_bytes_for(df_kind kind, uint32_t max_tile_elems) {
+  if (kind == DF_KIND_U4)  // range rounded down to 32 elements, the element after it, slack, rounded to 32
+    return ((max_tile_elems + 31 + 1 + kSlack + 31) & ~31u) + 32;
   // tile range rounded down to a 16-element granule, plus the slack of the
   // last lane's lookahead writes, rounded to 16, plus one spare granule
   return ((max_tile_elems + 15 + kSlack + 15) & ~15u) + 16;
@@ -605,7 +677,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
       if (v.n_luts > max_luts) max_luts = v.n_luts;
     }
     if (nj == 0) continue;
-    const uint32_t out_bytes = out_bytes_for(max_elems);
+    const uint32_t out_bytes = out_bytes_for(kind, max_elems);
     const uint32_t lut_bytes = max_luts * 512;
     // tile groups per workgroup: the choice that keeps the most waves
     // resident per CU (LDS is the limit: the tables are shared per workgroup)

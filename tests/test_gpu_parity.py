@@ -312,6 +312,23 @@ def test_llama3_8b_block_u8(torch_dev, orc):
     assert np.array_equal(got, orc.decode_tiles(oracle_container(cs[4]), 16))
 
 
+def test_llama3_8b_block_u4(torch_dev, orc):
+    """The 4-bit EntroLLM-style block: seven per-layer uint4 containers, one
+    batched launch, packed outputs."""
+    torch, dev = torch_dev
+    layers = synth.u4_block(0)
+    cs = [dfh.compress(dfh.KIND_U4, p, n=n) for _, p, n, _ in layers]
+    dcs = [dfh.to_device(c, dev) for c in cs]
+    outs = [dc.empty_output() for dc in dcs]
+    dfh.df_decompress_batch(dcs, outs)
+    torch.cuda.synchronize()
+    for (name, p, n, _), o in zip(layers, outs):
+        say("u4 layer", name)
+        assert torch.equal(o, torch.from_numpy(p).to(dev))
+    got = host_of(outs[4], 2)
+    assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(cs[4]), 16)))
+
+
 def test_offsets_beyond_2_pow_31(torch_dev):
     """Element indices and tile offsets at and above 2^31 (uint8, two symbols,
     one-bit codes: 2^31 + 2^20 + 37 weights, 2.2 GB)."""
@@ -329,3 +346,61 @@ def test_offsets_beyond_2_pow_31(torch_dev):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     assert torch.equal(out, torch.from_numpy(src).to(dev))
+
+
+# ------------------------------------------------------------------- uint4
+def u4_symbols(n, seed, std=2.2):
+    return np.clip(np.rint(np.random.default_rng(seed).normal(7.5, std, n)), 0, 15).astype(np.uint8)
+
+
+def check_u4(torch_dev, orc, q, checked=True):
+    """q: one symbol 0..15 per element.  The decoder's packed output must equal
+    the packed input and the oracle's packed decode of the same container."""
+    n = q.size
+    packed = synth.pack_u4(q)
+    c = dfh.compress(dfh.KIND_U4, packed, n=n)
+    got, err = gpu_decode(torch_dev, c, checked)
+    assert err == 0
+    assert got.size == (n + 1) // 2
+    assert np.array_equal(got, packed)
+    assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
+    return c
+
+
+@pytest.mark.parametrize("n", EDGE_SIZES)
+def test_u4_edge_sizes(torch_dev, orc, n):
+    say("u4 edge", n)
+    check_u4(torch_dev, orc, u4_symbols(n, n))
+
+
+def test_u4_odd_tile_boundaries(torch_dev, orc):
+    # many tiles: about half end on an odd element, sharing an output byte
+    # with the next tile, and of those some take the next symbol from the
+    # last lookup's lookahead and some decode it separately
+    for seed, std in ((1, 2.2), (2, 0.9), (3, 4.0)):
+        q = u4_symbols(3_000_001, seed, std)
+        c = check_u4(torch_dev, orc, q)
+        to = np.asarray(c.section("tile_out")).astype(np.int64)
+        assert (to[1:-1] % 2 == 1).sum() > 50
+
+
+def test_u4_long_codes_and_single_symbol(torch_dev, orc):
+    # geometric-like counts give codes up to 15 bits (past the 12-bit table)
+    rng = np.random.default_rng(9)
+    q = np.minimum(rng.geometric(0.55, 2_000_000) - 1, 15).astype(np.uint8)
+    c = check_u4(torch_dev, orc, q)
+    assert c.info()["lengths"].max() > 12
+    for n in (1, 2, 3, 16385, 40001):
+        check_u4(torch_dev, orc, np.full(n, 5, np.uint8))
+
+
+def test_u4_batch_and_checked(torch_dev, orc):
+    torch, dev = torch_dev
+    layers = synth.u4_block(0, shapes=synth.scaled_shapes(synth.LLAMA3_8B_BLOCK, 8))
+    cs = [dfh.compress(dfh.KIND_U4, p, n=n) for _, p, n, _ in layers]
+    dcs = [dfh.to_device(c, dev) for c in cs]
+    outs = [dc.empty_output() for dc in dcs]
+    dfh.df_decompress_batch(dcs, outs)
+    torch.cuda.synchronize()
+    for (_, p, n, _), o in zip(layers, outs):
+        assert np.array_equal(host_of(o, 2), p)
