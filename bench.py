@@ -49,13 +49,15 @@ def algorithmic_bytes(inf) -> int:
     if int(inf["kind"]) == 0:
         read += n
         write = 2 * n
-    else:
+    elif int(inf["kind"]) == 1:
         write = n
+    else:                       # uint4, packed two per byte
+        write = (n + 1) // 2
     return read + write
 
 
 WORKLOADS = ("llama3_8b_block_bf16", "c1_1m_bf16", "llama3_8b_block_u8", "llama3_8b_32_blocks_bf16",
-             "llama31_405b_block_t3_bf16", "llama3_8b_lm_head_bf16")
+             "llama31_405b_block_t3_bf16", "llama3_8b_lm_head_bf16", "llama3_8b_block_u4")
 
 
 def make_workload(name: str, seed: int):
@@ -86,11 +88,34 @@ def make_workload(name: str, seed: int):
                                   dist="t3")
         return 0, [src], {"matrices": "q,k,v,o,gate,up,down", "shapes": "Llama-3.1-405B block",
                           "dist": "Student-t(3)*0.02/sqrt(3)"}, "one"
+    if name == "llama3_8b_block_u4":
+        layers = synth.u4_block(seed)
+        return 2, [(p, n) for _, p, n, _ in layers], {
+            "matrices": "q,k,v,o,gate,up,down", "packing": "two per byte, low nibble first",
+            "quantizers": "".join("A" if a else "U" for _, _, _, a in layers)}, "batch"
     if name == "llama3_8b_lm_head_bf16":
         src, _ = synth.bf16_block(seed, config=synth.CONFIG_LM_HEAD, shapes=synth.LLAMA3_8B_LM_HEAD)
         return 0, [src], {"matrices": "lm_head", "shapes": "128256x4096, one matrix, one codebook",
                           "dist": "N(0,s^2), s~U[0.01,0.04]"}, "one"
     raise SystemExit("unknown workload " + name)
+
+
+def src_elems(kind, s) -> int:
+    """Elements of one workload source (uint4 sources are (packed, n))."""
+    return int(s[1]) if kind == 2 else int(s.size)
+
+
+def src_compress(dfh, kind, s):
+    return dfh.compress(kind, s[0], n=s[1]) if kind == 2 else dfh.compress(kind, s)
+
+
+def src_expected(kind, s) -> np.ndarray:
+    """The bytes the decoder must write for one source."""
+    return s[0] if kind == 2 else s.view(np.int16) if kind == 0 else s
+
+
+def out_bytes_of(kind, n) -> int:
+    return 2 * n if kind == 0 else n if kind == 1 else (n + 1) // 2
 
 
 def cpu_baseline(containers, srcs, kind):
@@ -102,7 +127,7 @@ def cpu_baseline(containers, srcs, kind):
         total += int(containers[keep].info()["n"])
         keep += 1
     containers, srcs = containers[:keep], srcs[:keep]
-    out_bytes = total * (2 if kind == 0 else 1)
+    out_bytes = sum(out_bytes_of(kind, int(c.info()["n"])) for c in containers)
     dicts = []
     for c in containers:
         inf = c.info()
@@ -110,12 +135,22 @@ def cpu_baseline(containers, srcs, kind):
         d.update(kind=inf["kind"], n=inf["n"], n_tiles=inf["n_tiles"], n_threads=inf["n_threads"],
                  lengths=inf["lengths"])
         dicts.append(d)
+    def decode(d, threads):   # the oracle's full output (uint4 packed by the oracle)
+        o = oracle.decode_tiles(d, threads)
+        return oracle.pack_u4(o) if kind == 2 else o
+
+    def expect(s, n=None):
+        e = src_expected(kind, s)
+        if n is None:
+            return e
+        return e[: (n + 1) // 2] if kind == 2 else e[:n]
+
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        outs = [oracle.decode_tiles(d, cores) for d in dicts]
+        outs = [decode(d, cores) for d in dicts]
         times.append(time.perf_counter() - t0)
-    ok = all(np.array_equal(o, s) for o, s in zip(outs, srcs))
+    ok = all(np.array_equal(o.view(np.uint8), expect(s).view(np.uint8)) for o, s in zip(outs, srcs))
     t_mt = statistics.median(times)
     # one thread on the first sixteenth of the tiles of the first container
     d0 = dict(dicts[0])
@@ -124,17 +159,20 @@ def cpu_baseline(containers, srcs, kind):
     d0["n"] = int(d0["tile_out"][nt])
     d0["tile_out"] = d0["tile_out"][: nt + 1]
     t0 = time.perf_counter()
-    o1 = oracle.decode_tiles(d0, 1)
+    o1 = decode(d0, 1)
     t_1 = time.perf_counter() - t0
-    ok = ok and np.array_equal(o1, srcs[0][: d0["n"]])
-    esz = 2 if kind == 0 else 1
+    if kind == 2 and d0["n"] % 2:   # a cut inside a byte: compare whole bytes only
+        o1 = o1[:-1]
+        ok = ok and np.array_equal(o1, expect(srcs[0], d0["n"] - 1))
+    else:
+        ok = ok and np.array_equal(o1.view(np.uint8), expect(srcs[0], d0["n"]).view(np.uint8))
     return {
         "value": round(out_bytes / t_mt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
         "sample": "%d of the workload's containers (%d elements), oracle bit-serial decode over "
                   "contiguous tile ranges on %d threads, median of 3 runs; single-thread figure on "
                   "the first 1/16 of the first container's tiles (%d elements)"
                   % (keep, total, cores, d0["n"]),
-        "value_1thread": round(d0["n"] * esz / t_1 / 1e9, 4), "verified": bool(ok),
+        "value_1thread": round(out_bytes_of(kind, d0["n"]) / t_1 / 1e9, 4), "verified": bool(ok),
         "cpu_model": cpu_model(),
     }
 
@@ -190,9 +228,9 @@ def main():
 
     log("workload", args.workload, "seed", args.seed)
     kind, srcs, wconf, mode = make_workload(args.workload, args.seed)
-    n = sum(s.size for s in srcs)
+    n = sum(src_elems(kind, s) for s in srcs)
     t0 = time.perf_counter()
-    containers = [dfh.compress(kind, s) for s in srcs]
+    containers = [src_compress(dfh, kind, s) for s in srcs]
     log("compressed in %.2f s" % (time.perf_counter() - t0))
     infos = [c.info() for c in containers]
     # one copy when the inputs alone exceed the 256 MB Infinity Cache many times
@@ -246,11 +284,11 @@ def main():
     else:
         for o in outs:
             for s, t in zip(srcs, o):
-                ref = torch.from_numpy(s.view(np.int16) if kind == 0 else s).to(dev)
+                ref = torch.from_numpy(src_expected(kind, s)).to(dev)
                 got = t.view(torch.int16) if kind == 0 else t
                 verified = verified and bool(torch.equal(got, ref))
 
-    out_bytes = n * (2 if kind == 0 else 1)
+    out_bytes = sum(out_bytes_of(kind, src_elems(kind, s)) for s in srcs)
     value = out_bytes * args.steps / wall / 1e9
     mean_ms = statistics.mean(launch_ms)
     alg = sum(algorithmic_bytes(i) for i in infos) / per_step  # per launch
@@ -267,13 +305,14 @@ def main():
             traffic = None
     line = {
         "metric": METRIC if args.workload == "llama3_8b_block_bf16" else
-        METRIC.replace("8B-shaped transformer block", args.workload),
+        ("decompressed %s GB/s (+%% of HBM roofline), %s"
+         % (("BF16", "uint8", "packed uint4")[kind], args.workload)),
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
         "data": "synthetic",
         "config": dict({"workload": args.workload, "elements": int(n), "containers": len(containers),
-                        "output": "bf16" if kind == 0 else "uint8", "seed": args.seed,
+                        "output": ("bf16", "uint8", "uint4 packed")[kind], "seed": args.seed,
                         "stored_bytes": int(stored), "stored_over_raw": round(stored / out_bytes, 4),
                         "input_copies": len(copies), "launches_per_step": per_step}, **wconf),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
