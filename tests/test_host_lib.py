@@ -230,3 +230,20 @@ def test_forward_block_shape_matches_benchmark_block():
     from lossless_entropy_coded_huffman_amd import forward as fw, synth
     assert fw.LLAMA3_8B.matrices() == synth.LLAMA3_8B_BLOCK
     assert fw.LLAMA3_8B.elements() == synth.block_elems(synth.LLAMA3_8B_BLOCK) == 218_103_808
+
+
+def test_encode_rejects_more_tables_than_the_cap(orc):
+    # 96 codes of 7 bits and 128 of 9 bits (Kraft sum exactly 1): the 9-bit
+    # codes spread over 64 distinct 8-bit prefixes, each needing a second
+    # level table, so the code needs 65 tables (cap 64)
+    ln = np.zeros(256, np.uint8)
+    ln[:96] = 7
+    ln[96:224] = 9
+    assert sum(2.0 ** -int(l) for l in ln if l) == 1.0
+    with pytest.raises(ValueError):
+        orc.build_lut(ln, cap=64)
+    assert orc.build_lut(ln, cap=65)[1] == 65
+    src = np.arange(224, dtype=np.uint8)
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_encode(dfh.KIND_U8, src, ln)
+    assert e.value.status == -3
