@@ -229,6 +229,54 @@ df_status df_decompress_checked(const df_device_view *v, void *dst, uint32_t *d_
 df_status df_decompress_batch(const df_device_view *views, void *const *dsts, uint32_t count,
                               hipStream_t stream);
 
+/* ------------------------------------------------------- device encoding */
+
+/* Encoding on the GPU, for weights already in device memory (fast
+ * conversion of a checkpoint; the pages encode offline and describe no
+ * encoder kernel, so this part is this library's own).  The sections it
+ * writes are byte-identical to df_encode's.  Steps:
+ *   1. df_histogram_device, then copy the 256 counts to the host;
+ *   2. df_build_codebook on the host;
+ *   3. df_encode_layout for the sizes, df_build_tables for LUT and DTAB;
+ *   4. allocate the device sections and df_encode_workspace_bytes(n) bytes
+ *      of device workspace, copy LUT and DTAB, then df_encode_device.
+ * Device calls enqueue on the stream and return, as for decompression. */
+
+/* Histogram of the coded symbols of n device elements (layout as for
+ * df_histogram) into d_hist, 256 device uint64 counts; the call clears them
+ * first.  DF_ERR_ARG on a null pointer or bad kind. */
+df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint64_t *d_hist,
+                              hipStream_t stream);
+
+/* Header scalars and section sizes of the container df_encode would build
+ * for n elements with this histogram and these lengths, whose last element
+ * has symbol last_symbol (max_tile_elems is left 0: df_encode_device
+ * reports it).  DF_ERR_CODEBOOK when a counted symbol has no code or the
+ * lengths break Kraft's inequality; DF_ERR_ARG on a bad argument. */
+df_status df_encode_layout(df_kind kind, uint64_t n, const uint64_t hist[256], uint8_t last_symbol,
+                           const uint8_t lengths[256], df_info *out);
+
+/* The derived decode tables for these lengths: lut (room for lut_cap
+ * 256-entry levels) with *n_luts levels used, and dtab (4096 entries), as in
+ * the container sections LUT and DTAB.  DF_ERR_CODEBOOK when more than
+ * lut_cap levels are needed. */
+df_status df_build_tables(df_kind kind, const uint8_t lengths[256], uint16_t *lut, uint32_t lut_cap,
+                          uint32_t *n_luts, uint64_t *dtab);
+
+/* Device workspace bytes df_encode_device needs for n elements. */
+uint64_t df_encode_workspace_bytes(uint64_t n);
+
+/* Encode n device elements into device sections sized by df_encode_layout
+ * (layout is its result): bitstream, gaps, tile_out and, for BF16,
+ * sign_mantissa (NULL otherwise).  d_workspace: df_encode_workspace_bytes(n)
+ * bytes, 16-byte aligned.  d_max_tile (one device uint32) receives
+ * max_tile_elems.  Each element's code goes at the sum of the lengths of
+ * the codes before it (a scan of code lengths over the elements). */
+df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                           const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
+                           uint64_t *d_tile_out, uint8_t *d_sign_mantissa, void *d_workspace,
+                           uint32_t *d_max_tile, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,9 +37,12 @@ def build() -> str:
           "-D__HIP_PLATFORM_AMD__"] + inc + ["-c", os.path.join(CSRC, "dfh_host.cpp"), "-o", host_o])
     _run([os.path.join(ROCM, "bin", "hipcc")] + HIP_FLAGS + inc +
          ["-c", os.path.join(CSRC, "dfh_decode.hip"), "-o", dev_o])
+    enc_o = os.path.join(BUILD, "dfh_encode.o")
+    _run([os.path.join(ROCM, "bin", "hipcc")] + HIP_FLAGS + inc +
+         ["-c", os.path.join(CSRC, "dfh_encode.hip"), "-o", enc_o])
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([os.path.join(ROCM, "bin", "hipcc"), "-shared", "-fPIC", "--offload-arch=" + ARCH,
-          host_o, dev_o, "-pthread", "-o", tmp])
+          host_o, dev_o, enc_o, "-pthread", "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

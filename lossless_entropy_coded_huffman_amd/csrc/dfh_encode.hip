@@ -1,0 +1,323 @@
+// dfh_encode.hip -- device-side encoder for gfx950 (MI355X).
+//
+// Produces the same container sections as the host encoder, from elements
+// already in device memory.  The pages encode offline and describe no
+// encoder kernel; the format it fills is the one the DFloat11 digest
+// ("DFloat11: compressao sem perda para inferencia em GPU...", sections
+// "O formato DFloat11" and "Kernel de GPU em 2 etapas e metadados
+// auxiliares") describes: codes concatenated into one stream, a 5-bit gap
+// per 64-bit chunk (where its first code starts), one output index per
+// 16384-bit tile, and for BF16 the packed sign|mantissa bytes.
+//
+// Each element's code starts at the sum of the lengths of the codes before
+// it.  That sum is a scan over the elements, done in three launches:
+//   enc_sums   one workgroup per block of kBlock elements sums its lengths;
+//   enc_scan   one workgroup turns the block sums into block start bits;
+//   enc_write  each workgroup rescans its block, packs its codes into an
+//              LDS bit buffer and writes it out (interior words with plain
+//              stores; the first and last words, shared with the
+//              neighbouring blocks, with atomic ORs into the zeroed stream),
+//              and writes the gap field of every chunk and the offset of
+//              every tile in which one of its codes is the first to start.
+// enc_finish then writes tile_out[n_tiles] = n and the largest tile.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "dfh.h"
+
+namespace {
+
+constexpr uint32_t kThreads = 256;                 // encoder workgroup
+constexpr uint32_t kPerThread = 16;                // consecutive elements per thread
+constexpr uint32_t kBlock = kThreads * kPerThread;  // elements per block
+constexpr uint32_t kGapBits = 5;
+
+struct Codebook {
+  uint32_t rev[256];  // code with its first bit at bit 0 (stream order)
+  uint8_t len[256];   // 0 = no code
+};
+
+__device__ __forceinline__ uint32_t symbol_at(int kind, const void *src, uint64_t i) {
+  if (kind == DF_KIND_BF16) return (((const uint16_t *)src)[i] >> 7) & 0xFFu;
+  if (kind == DF_KIND_U4) return (((const uint8_t *)src)[i >> 1] >> (4 * (uint32_t)(i & 1))) & 0xFu;
+  return ((const uint8_t *)src)[i];
+}
+
+__global__ void fill_zero(uint32_t *p, uint64_t words) {
+  for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void histogram_kernel(int kind, const void *src, uint64_t n,
+                                                             unsigned long long *hist) {
+  __shared__ uint32_t h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kThreads)
+    atomicAdd(&h[symbol_at(kind, src, i)], 1u);
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], (unsigned long long)h[threadIdx.x]);
+}
+
+// Sum of the workgroup's 256 values, returned to every thread.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *scratch) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t s = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+  __syncthreads();
+  return s;
+}
+
+// Exclusive prefix sum of the workgroup's 256 values in thread order.
+__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t *scratch) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= (uint32_t)o) x += y;
+  }
+  if (lane == 63) scratch[w] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  for (uint32_t k = 0; k < w; k++) before += scratch[k];
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void enc_sums(int kind, const void *src, uint64_t n, Codebook cb,
+                                                     uint64_t *block_sums) {
+  __shared__ uint8_t len[256];
+  __shared__ uint32_t scratch[4];
+  len[threadIdx.x] = cb.len[threadIdx.x];
+  __syncthreads();
+  const uint64_t b0 = (uint64_t)blockIdx.x * kBlock;
+  uint32_t s = 0;
+  for (uint32_t k = 0; k < kPerThread; k++) {
+    const uint64_t i = b0 + (uint64_t)k * kThreads + threadIdx.x;
+    if (i < n) s += len[symbol_at(kind, src, i)];
+  }
+  s = block_sum(s, scratch);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = s;
+}
+
+// One workgroup: block_base[b] = sum of block_sums[0 .. b).
+__global__ __launch_bounds__(1024) void enc_scan(const uint64_t *block_sums, uint64_t nblocks,
+                                                 uint64_t *block_base) {
+  __shared__ uint64_t part[1024];
+  const uint64_t per = (nblocks + 1023) / 1024;
+  const uint64_t b = threadIdx.x * per, e = b + per < nblocks ? b + per : nblocks;
+  uint64_t s = 0;
+  for (uint64_t i = b; i < e; i++) s += block_sums[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {  // 1024 partial sums, sequentially
+    uint64_t run = 0;
+    for (int t = 0; t < 1024; t++) {
+      const uint64_t v = part[t];
+      part[t] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  uint64_t run = part[threadIdx.x];
+  for (uint64_t i = b; i < e; i++) {
+    const uint64_t v = block_sums[i];
+    block_base[i] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src, uint64_t n, Codebook cb,
+                                                      const uint64_t *block_base, uint32_t *bits,
+                                                      uint32_t *gaps, uint64_t *tile_out, uint8_t *sm) {
+  __shared__ uint32_t rev[256];
+  __shared__ uint8_t len[256];
+  __shared__ uint32_t scratch[4];
+  // the block's codes, from the word its first bit falls in: at most
+  // kBlock * 32 bits starting up to 31 bits into word 0, so words 0..kBlock
+  __shared__ uint32_t buf[kBlock + 1];
+  rev[threadIdx.x] = cb.rev[threadIdx.x];
+  len[threadIdx.x] = cb.len[threadIdx.x];
+  for (uint32_t k = threadIdx.x; k < kBlock + 1; k += kThreads) buf[k] = 0;
+  __syncthreads();
+
+  const uint64_t b0 = (uint64_t)blockIdx.x * kBlock;
+  const uint64_t i0 = b0 + (uint64_t)threadIdx.x * kPerThread;  // this thread's first element
+  uint32_t syms[kPerThread];
+  uint32_t mine = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < kPerThread; k++) {
+    syms[k] = i0 + k < n ? symbol_at(kind, src, i0 + k) : 0u;
+    mine += i0 + k < n ? len[syms[k]] : 0u;
+  }
+  const uint64_t base = block_base[blockIdx.x];
+  const uint64_t word0 = base >> 5;  // global word of the block's first bit
+  uint64_t pos = base + block_exclusive(mine, scratch);
+  // start of the element before this thread's first one
+  uint64_t prev = 0;
+  if (i0 > 0 && i0 < n) prev = pos - len[symbol_at(kind, src, i0 - 1)];
+
+#pragma unroll
+  for (uint32_t k = 0; k < kPerThread; k++) {
+    const uint64_t i = i0 + k;
+    if (i >= n) break;
+    const uint32_t s = syms[k], l = len[s];
+    if (i == 0) {
+      tile_out[0] = 0;  // gap field 0 is 0: the stream is cleared beforehand
+    } else {
+      if ((prev >> 6) != (pos >> 6)) {  // first code of chunk pos / 64
+        const uint64_t t = pos >> 6, g = pos & 63, at = t * kGapBits;
+        const uint32_t sh = (uint32_t)(at & 31);
+        atomicOr(&gaps[at >> 5], (uint32_t)(g << sh));
+        if (sh > 32 - kGapBits) atomicOr(&gaps[(at >> 5) + 1], (uint32_t)(g >> (32 - sh)));
+      }
+      if ((prev >> 14) != (pos >> 14)) tile_out[pos >> 14] = i;  // first code of tile pos / 16384
+    }
+    // the code's bits into the block buffer: at most two words
+    const uint64_t lp = pos - (word0 << 5);
+    const uint32_t w = (uint32_t)(lp >> 5), sh = (uint32_t)(lp & 31);
+    const uint64_t v = (uint64_t)rev[s] << sh;
+    atomicOr(&buf[w], (uint32_t)v);
+    if ((uint32_t)(v >> 32)) atomicOr(&buf[w + 1], (uint32_t)(v >> 32));
+    prev = pos;
+    pos += l;
+  }
+  if (kind == DF_KIND_BF16) {  // sign|mantissa bytes of this thread's elements
+    const uint16_t *u = (const uint16_t *)src;
+    if (i0 + kPerThread <= n) {
+      uint32_t o[kPerThread / 4];
+#pragma unroll
+      for (uint32_t q = 0; q < kPerThread / 4; q++) {
+        uint32_t x = 0;
+#pragma unroll
+        for (uint32_t r = 0; r < 4; r++) {
+          const uint32_t e = u[i0 + 4 * q + r];
+          x |= (((e >> 8) & 0x80u) | (e & 0x7Fu)) << (8 * r);
+        }
+        o[q] = x;
+      }
+      *(uint4 *)(sm + i0) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (uint64_t i = i0; i < n; i++) sm[i] = (uint8_t)(((u[i] >> 8) & 0x80u) | (u[i] & 0x7Fu));
+    }
+  }
+  __syncthreads();
+
+  // out: the block's bit range [base, base + its lengths) as words word0 ..
+  const uint64_t last_bit = base + block_sum(mine, scratch);
+  if (last_bit == base) return;
+  const uint64_t nwords = ((last_bit + 31) >> 5) - word0;
+  for (uint64_t k = threadIdx.x; k < nwords; k += kThreads) {
+    const uint32_t v = buf[k];
+    const bool edge = k == 0 || k == nwords - 1;  // shared with the block before or after
+    if (edge) {
+      if (v) atomicOr(&bits[word0 + k], v);
+    } else {
+      bits[word0 + k] = v;
+    }
+  }
+}
+
+__global__ void enc_finish(uint64_t *tile_out, uint64_t n_tiles, uint64_t n, uint32_t *max_tile) {
+  for (uint64_t b = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; b < n_tiles;
+       b += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t hi = b + 1 == n_tiles ? n : tile_out[b + 1];
+    atomicMax(max_tile, (uint32_t)(hi - tile_out[b]));
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) tile_out[n_tiles] = n;
+}
+
+uint64_t blocks_for(uint64_t n) { return (n + kBlock - 1) / kBlock; }
+
+}  // namespace
+
+extern "C" {
+
+df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint64_t *d_hist,
+                              hipStream_t stream) {
+  if (!d_hist || (n && !d_src) || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4))
+    return DF_ERR_ARG;
+  hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, stream, (uint32_t *)d_hist, (uint64_t)512);
+  if (n) {
+    uint64_t grid = (n + kThreads * 64 - 1) / (kThreads * 64);
+    if (grid > 4096) grid = 4096;
+    hipLaunchKernelGGL(histogram_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, (int)kind, d_src, n,
+                       (unsigned long long *)d_hist);
+  }
+  return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+uint64_t df_encode_workspace_bytes(uint64_t n) { return 2 * 8 * (blocks_for(n) + 1) + 16; }
+
+df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                           const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
+                           uint64_t *d_tile_out, uint8_t *d_sign_mantissa, void *d_workspace,
+                           uint32_t *d_max_tile, hipStream_t stream) {
+  if (!lengths || !layout || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4) ||
+      layout->kind != kind || layout->n != n || !d_tile_out || !d_max_tile)
+    return DF_ERR_ARG;
+  if (n && (!d_src || !d_bitstream || !d_gaps || !d_workspace || ((uintptr_t)d_workspace & 15) ||
+            ((uintptr_t)d_bitstream & 15) || ((uintptr_t)d_gaps & 15) || ((uintptr_t)d_tile_out & 7)))
+    return DF_ERR_ARG;
+  if (kind == DF_KIND_BF16 && n && (!d_sign_mantissa || ((uintptr_t)d_sign_mantissa & 15))) return DF_ERR_ARG;
+  if (memcmp(layout->lengths, lengths, 256) != 0) return DF_ERR_ARG;
+  // the canonical code of every length (RFC 1951 3.2.2), bit-reversed into
+  // stream order
+  Codebook cb;
+  memset(&cb, 0, sizeof cb);
+  {
+    uint32_t count[DF_MAX_LEN + 2] = {0}, next[DF_MAX_LEN + 2] = {0};
+    for (int s = 0; s < 256; s++)
+      if (lengths[s]) {
+        if (lengths[s] > DF_MAX_LEN) return DF_ERR_CODEBOOK;
+        count[lengths[s]]++;
+      }
+    uint64_t code = 0;
+    for (int l = 1; l <= DF_MAX_LEN; l++) {
+      code = (code + count[l - 1]) << 1;
+      next[l] = (uint32_t)code;
+    }
+    for (int s = 0; s < 256; s++) {
+      const uint32_t l = lengths[s];
+      cb.len[s] = (uint8_t)l;
+      if (!l) continue;
+      const uint32_t c = next[l]++;
+      uint32_t r = 0;
+      for (uint32_t k = 0; k < l; k++) r |= ((c >> (l - 1 - k)) & 1u) << k;
+      cb.rev[s] = r;
+    }
+  }
+  const uint64_t n_tiles = layout->n_tiles;
+  hipLaunchKernelGGL(fill_zero, dim3(1), dim3(32), 0, stream, d_max_tile, (uint64_t)1);
+  if (n == 0) {
+    hipLaunchKernelGGL(enc_finish, dim3(1), dim3(64), 0, stream, d_tile_out, (uint64_t)0, (uint64_t)0,
+                       d_max_tile);
+    return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
+  }
+  const uint64_t zb = layout->section_bytes[DF_SEC_BITSTREAM] / 4, zg = layout->section_bytes[DF_SEC_GAPS] / 4;
+  hipLaunchKernelGGL(fill_zero, dim3(1024), dim3(256), 0, stream, (uint32_t *)d_bitstream, zb);
+  hipLaunchKernelGGL(fill_zero, dim3(64), dim3(256), 0, stream, (uint32_t *)d_gaps, zg);
+  if (kind == DF_KIND_BF16) {  // the padding past n
+    const uint64_t pad0 = n & ~(uint64_t)63, words = (layout->section_bytes[DF_SEC_SIGN_MANTISSA] - pad0) / 4;
+    hipLaunchKernelGGL(fill_zero, dim3(1), dim3(64), 0, stream, (uint32_t *)(d_sign_mantissa + pad0), words);
+  }
+  const uint64_t nb = blocks_for(n);
+  if (nb > 0xFFFFFFFFull) return DF_ERR_ARG;
+  uint64_t *sums = (uint64_t *)d_workspace, *bases = sums + nb + 1;
+  hipLaunchKernelGGL(enc_sums, dim3((uint32_t)nb), dim3(kThreads), 0, stream, (int)kind, d_src, n, cb, sums);
+  hipLaunchKernelGGL(enc_scan, dim3(1), dim3(1024), 0, stream, (const uint64_t *)sums, nb, bases);
+  hipLaunchKernelGGL(enc_write, dim3((uint32_t)nb), dim3(kThreads), 0, stream, (int)kind, d_src, n, cb,
+                     (const uint64_t *)bases, (uint32_t *)d_bitstream, (uint32_t *)d_gaps, d_tile_out,
+                     d_sign_mantissa);
+  uint64_t grid = (n_tiles + 255) / 256;
+  if (grid < 1) grid = 1;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(enc_finish, dim3((uint32_t)grid), dim3(256), 0, stream, d_tile_out, n_tiles, n, d_max_tile);
+  return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+}  // extern "C"

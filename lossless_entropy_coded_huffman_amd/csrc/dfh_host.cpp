@@ -511,6 +511,53 @@ df_status df_encode(df_kind kind, const void *src, uint64_t n, const uint8_t len
   return DF_OK;
 }
 
+df_status df_encode_layout(df_kind kind, uint64_t n, const uint64_t hist[256], uint8_t last_symbol,
+                           const uint8_t lengths[256], df_info *out) {
+  if (!hist || !lengths || !out || !valid_kind(kind)) return DF_ERR_ARG;
+  uint64_t kr = kraft_scaled(lengths);
+  if (kr == UINT64_MAX || kr > (1ull << 32)) return DF_ERR_CODEBOOK;
+  uint64_t total_bits = 0, counted = 0;
+  for (int s = 0; s < 256; s++) {
+    if (!hist[s]) continue;
+    if (!lengths[s]) return DF_ERR_CODEBOOK;
+    total_bits += hist[s] * lengths[s];
+    counted += hist[s];
+  }
+  if (counted != n || (n && (!hist[last_symbol] || !lengths[last_symbol]))) return DF_ERR_ARG;
+  df_container c;  // header arithmetic only: no section is allocated
+  c.info.kind = kind;
+  memcpy(c.info.lengths, lengths, 256);
+  set_layout(&c, n, total_bits, n ? total_bits - lengths[last_symbol] : 0);
+  std::vector<uint16_t> lut;
+  const int nl = build_tables(lengths, lut);
+  if (nl < 0) return DF_ERR_CODEBOOK;
+  df_info &in = c.info;
+  in.n_luts = (uint32_t)nl;
+  in.max_tile_elems = 0;
+  in.section_bytes[DF_SEC_BITSTREAM] = in.n_tiles * (DF_TILE_BITS / 8) + 16;
+  in.section_bytes[DF_SEC_GAPS] = in.n_tiles * kGapBytesPerTile + 16;
+  in.section_bytes[DF_SEC_TILE_OUT] = (in.n_tiles + 1) * 8;
+  in.section_bytes[DF_SEC_SIGN_MANTISSA] = kind == DF_KIND_BF16 ? round_up(n, 64) : 0;
+  in.section_bytes[DF_SEC_LUT] = lut.size() * 2;
+  in.section_bytes[DF_SEC_DTAB] = (uint64_t)kDtabSize * 8;
+  *out = in;
+  return DF_OK;
+}
+
+df_status df_build_tables(df_kind kind, const uint8_t lengths[256], uint16_t *lut, uint32_t lut_cap,
+                          uint32_t *n_luts, uint64_t *dtab) {
+  if (!lengths || !lut || !n_luts || !dtab || !valid_kind(kind)) return DF_ERR_ARG;
+  std::vector<uint16_t> l;
+  const int nl = build_tables(lengths, l);
+  if (nl < 0 || (uint32_t)nl > lut_cap) return DF_ERR_CODEBOOK;
+  memcpy(lut, l.data(), l.size() * 2);
+  *n_luts = (uint32_t)nl;
+  std::vector<uint64_t> d;
+  build_dtab(kind, l, d);
+  memcpy(dtab, d.data(), d.size() * 8);
+  return DF_OK;
+}
+
 df_status df_container_info(const df_container *c, df_info *out) {
   if (!c || !out) return DF_ERR_ARG;
   *out = c->info;

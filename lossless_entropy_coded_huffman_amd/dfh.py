@@ -58,6 +58,16 @@ _lock = threading.Lock()
 
 # name -> (restype, argtypes); the exported C ABI
 _SIGNATURES = {
+    "df_histogram_device": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "df_encode_layout": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint8,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "df_build_tables": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.POINTER(ctypes.c_uint32), ctypes.c_void_p]),
+    "df_encode_workspace_bytes": (ctypes.c_uint64, [ctypes.c_uint64]),
+    "df_encode_device": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "df_histogram": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
     "df_build_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "df_encode": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
@@ -267,19 +277,23 @@ class DeviceContainer:
     """A container's sections copied to device memory (torch uint8 tensors)
     and the df_device_view that borrows them."""
 
-    def __init__(self, c: Container, device="cuda"):
-        inf = c.info()
+    def __init__(self, c: Container | None, device="cuda", _info=None, _sections=None):
+        if c is None:   # sections already on the device (compress_device)
+            inf, self.sections = _info, _sections
+            self.device = torch.device(device)
+        else:
+            inf = c.info()
+            self.device = torch.device(device)
+            self.sections = {}
+            for i, name in enumerate(SECTION_NAMES):
+                host = _section_bytes(c, i)
+                t = torch.empty(max(host.size, 16), dtype=torch.uint8, device=self.device)
+                if host.size:
+                    t[: host.size].copy_(torch.from_numpy(host), non_blocking=False)
+                self.sections[name] = t
         self.kind = int(inf["kind"])
         self.n = int(inf["n"])
         self.info = inf
-        self.device = torch.device(device)
-        self.sections = {}
-        for i, name in enumerate(SECTION_NAMES):
-            host = _section_bytes(c, i)
-            t = torch.empty(max(host.size, 16), dtype=torch.uint8, device=self.device)
-            if host.size:
-                t[: host.size].copy_(torch.from_numpy(host), non_blocking=False)
-            self.sections[name] = t
         v = df_device_view()
         v.kind = self.kind
         v.n_luts = inf["n_luts"]
@@ -308,6 +322,105 @@ class DeviceContainer:
 
 def to_device(c: Container, device="cuda") -> DeviceContainer:
     return DeviceContainer(c, device)
+
+
+# ------------------------------------------------------- device encoding
+def _info_dict(inf: df_info) -> dict:
+    d = {k: getattr(inf, k) for k, _ in df_info._fields_ if k not in ("section_bytes", "lengths")}
+    d["section_bytes"] = {name: int(inf.section_bytes[i]) for i, name in enumerate(SECTION_NAMES)}
+    d["lengths"] = np.frombuffer(bytes(inf.lengths), np.uint8).copy()
+    return d
+
+
+def _device_elements(kind: int, t: torch.Tensor, n) -> int:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = t.numel() * t.element_size()
+    if kind == KIND_BF16:
+        if t.element_size() != 2:
+            raise TypeError("BF16 input needs 2-byte elements")
+        return t.numel()
+    if t.element_size() != 1:
+        raise TypeError("uint8 / uint4 input is a byte tensor")
+    if kind == KIND_U8:
+        return nbytes
+    n = 2 * nbytes if n is None else int(n)
+    if n < 0 or (n + 1) // 2 > nbytes:
+        raise ValueError("uint4 input holds fewer than n elements")
+    return n
+
+
+def df_histogram_device(kind: int, src: torch.Tensor, n=None, stream=None) -> torch.Tensor:
+    """256 counts (a device int64 tensor holding uint64 values)."""
+    n = _device_elements(kind, src, n)
+    h = torch.empty(256, dtype=torch.int64, device=src.device)
+    _check(lib().df_histogram_device(kind, ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(h.data_ptr()),
+                                     _stream_handle(stream, src.device)), "df_histogram_device")
+    return h
+
+
+def df_encode_layout(kind: int, n: int, hist, last_symbol: int, lengths) -> df_info:
+    h = np.ascontiguousarray(hist, np.uint64)
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    out = df_info()
+    _check(lib().df_encode_layout(kind, int(n), h.ctypes.data, int(last_symbol), ln.ctypes.data,
+                                  ctypes.byref(out)), "df_encode_layout")
+    return out
+
+
+def df_build_tables(kind: int, lengths, lut_cap: int = 64):
+    """(lut uint16[n_luts * 256], n_luts, dtab uint64[4096])."""
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    lut = np.zeros(lut_cap * 256, np.uint16)
+    dtab = np.zeros(1 << 12, np.uint64)
+    nl = ctypes.c_uint32(0)
+    _check(lib().df_build_tables(kind, ln.ctypes.data, lut.ctypes.data, int(lut_cap), ctypes.byref(nl),
+                                 dtab.ctypes.data), "df_build_tables")
+    return lut[: nl.value * 256].copy(), nl.value, dtab
+
+
+def df_encode_workspace_bytes(n: int) -> int:
+    return int(lib().df_encode_workspace_bytes(int(n)))
+
+
+def df_encode_device(kind: int, src: torch.Tensor, n: int, lengths, layout: df_info, sections: dict,
+                     workspace: torch.Tensor, max_tile: torch.Tensor, stream=None):
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    ptr = lambda name: ctypes.c_void_p(sections[name].data_ptr())  # noqa: E731
+    sm = ptr("sign_mantissa") if kind == KIND_BF16 else None
+    _check(lib().df_encode_device(kind, ctypes.c_void_p(src.data_ptr()), int(n), ln.ctypes.data,
+                                  ctypes.byref(layout), ptr("bitstream"), ptr("gaps"), ptr("tile_out"), sm,
+                                  ctypes.c_void_p(workspace.data_ptr()), ctypes.c_void_p(max_tile.data_ptr()),
+                                  _stream_handle(stream, src.device)), "df_encode_device")
+
+
+def compress_device(kind: int, src: torch.Tensor, max_len: int = MAX_LEN, n=None, stream=None) -> DeviceContainer:
+    """Encode device-resident elements on the GPU: device histogram, codebook
+    and tables on the host, device encode.  The sections equal compress()'s.
+    For uint4, src is the packed bytes and n the element count."""
+    n = _device_elements(kind, src, n)
+    hist = df_histogram_device(kind, src, n, stream).cpu().numpy().view(np.uint64)
+    lengths = df_build_codebook(hist, max_len)
+    last = 0
+    if n:
+        if kind == KIND_BF16:
+            last = (int(src.view(torch.int16)[n - 1].item()) >> 7) & 0xFF
+        elif kind == KIND_U8:
+            last = int(src[n - 1].item())
+        else:
+            last = (int(src[(n - 1) // 2].item()) >> (4 * ((n - 1) & 1))) & 0xF
+    layout = df_encode_layout(kind, n, hist, last, lengths)
+    inf = _info_dict(layout)
+    sec = {name: torch.empty(max(inf["section_bytes"][name], 16), dtype=torch.uint8, device=src.device)
+           for name in SECTION_NAMES}
+    lut, _, dtab = df_build_tables(kind, lengths)
+    sec["lut"][: lut.nbytes].copy_(torch.from_numpy(lut.view(np.uint8)))
+    sec["dtab"][: dtab.nbytes].copy_(torch.from_numpy(dtab.view(np.uint8)))
+    ws = torch.empty(max(df_encode_workspace_bytes(n), 16), dtype=torch.uint8, device=src.device)
+    max_tile = torch.zeros(1, dtype=torch.int32, device=src.device)
+    df_encode_device(kind, src, n, lengths, layout, sec, ws, max_tile, stream)
+    inf["max_tile_elems"] = int(max_tile.item())
+    return DeviceContainer(None, src.device, _info=inf, _sections=sec)
 
 
 def _stream_handle(stream, device):

@@ -247,3 +247,25 @@ def test_encode_rejects_more_tables_than_the_cap(orc):
     with pytest.raises(dfh.DFError) as e:
         dfh.df_encode(dfh.KIND_U8, src, ln)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+@pytest.mark.parametrize("n", [0, 1, 65, 16385, 100_003])
+def test_encode_layout_and_tables_match_the_encoder(kind, n):
+    # the host calls that size a device encoding: same header scalars and
+    # section sizes as the encoder's container, same LUT and DTAB
+    src = inputs(kind, n, 7 + n)
+    nn = n if kind == dfh.KIND_U4 else None
+    c = dfh.compress(kind, src, n=nn)
+    inf = c.info()
+    h = dfh.df_histogram(kind, src, nn)
+    sym = decoded_of(kind, src, n) if kind != 0 else ((src.view(np.uint16) >> 7) & 0xFF)
+    lay = dfh.df_encode_layout(kind, n, h, int(sym[-1]) if n else 0, inf["lengths"])
+    for k in ("n", "total_bits", "n_threads", "n_tiles", "n_luts"):
+        assert getattr(lay, k) == inf[k], k
+    assert [int(x) for x in lay.section_bytes] == [inf["section_bytes"][k] for k in dfh.SECTION_NAMES]
+    if n:
+        lut, nl, dtab = dfh.df_build_tables(kind, inf["lengths"])
+        assert nl == inf["n_luts"]
+        assert np.array_equal(lut, np.asarray(c.section("lut")))
+        assert np.array_equal(dtab, np.asarray(c.section("dtab")))
