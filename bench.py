@@ -200,6 +200,9 @@ def main():
                     help="instead of the decode benchmark: a forward pass over this many "
                          "Llama-3-8B-shaped blocks, weights decoded one block ahead on a side "
                          "stream; prints the exposed decode time per block")
+    ap.add_argument("--encode", action="store_true",
+                    help="instead of the decode benchmark: encode the workload on the GPU and on "
+                         "the host, check the sections are identical, print both times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the codec, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -224,6 +227,9 @@ def main():
         return
     if args.forward:
         forward_overlap(torch, dev, args)
+        return
+    if args.encode:
+        encode_bench(torch, dev, args)
         return
 
     log("workload", args.workload, "seed", args.seed)
@@ -398,6 +404,76 @@ def forward_overlap(torch, dev, args):
                               "side stream; serial = each block decoded on the compute stream "
                               "before it runs"}), flush=True)
     if not ok:
+        sys.exit(1)
+
+
+def encode_bench(torch, dev, args):
+    """Device encoder (compress_device: device histogram, host codebook and
+    tables, device encode) against the host encoder (compress, all host
+    threads) on the workload's containers; sections must be identical."""
+    import lossless_entropy_coded_huffman_amd as dfh
+    kind, srcs, wconf, _ = make_workload(args.workload, args.seed)
+    n = sum(src_elems(kind, s) for s in srcs)
+    in_bytes = sum((s[0] if kind == 2 else s).nbytes for s in srcs)
+
+    def dev_tensor(s):
+        if kind == 0:
+            return torch.from_numpy(s.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(s[0] if kind == 2 else s).to(dev)
+
+    dsrc = [dev_tensor(s) for s in srcs]
+    nn = [s[1] if kind == 2 else None for s in srcs]
+    t0 = time.perf_counter()
+    host = [src_compress(dfh, kind, s) for s in srcs]
+    t_host = time.perf_counter() - t0
+    def last_symbol(s):
+        if kind == 0:
+            return (int(s.view(np.uint16)[-1]) >> 7) & 0xFF
+        if kind == 1:
+            return int(s[-1])
+        return (int(s[0][(s[1] - 1) // 2]) >> (4 * ((s[1] - 1) & 1))) & 0xF
+
+    lays = [dfh.df_encode_layout(kind, src_elems(kind, s),
+                                 dfh.df_histogram(kind, s[0] if kind == 2 else s, s[1] if kind == 2 else None),
+                                 last_symbol(s), h.info()["lengths"]) for s, h in zip(srcs, host)]
+    ws = [torch.empty(max(dfh.df_encode_workspace_bytes(src_elems(kind, s)), 16), dtype=torch.uint8, device=dev)
+          for s in srcs]
+    mt = torch.zeros(1, dtype=torch.int32, device=dev)
+    dcs = None
+    for _ in range(3):   # warm-up
+        dcs = [dfh.compress_device(kind, t, n=k) for t, k in zip(dsrc, nn)]
+    torch.cuda.synchronize()
+    e2e, kern = [], []
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(10):
+        t0 = time.perf_counter()
+        dcs = [dfh.compress_device(kind, t, n=k) for t, k in zip(dsrc, nn)]
+        torch.cuda.synchronize()
+        e2e.append(time.perf_counter() - t0)
+        # the encode kernels alone, into the same sections
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for dc, t, k, w, lay, h in zip(dcs, dsrc, nn, ws, lays, host):
+            dfh.df_encode_device(kind, t, dc.n, h.info()["lengths"], lay, dc.sections, w, mt, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        kern.append(a.elapsed_time(b) * 1e-3)
+    same = all(np.array_equal(dc.sections[name][: h.info()["section_bytes"][name]].cpu().numpy(),
+                              np.asarray(h.section(name)).view(np.uint8))
+               for dc, h in zip(dcs, host) for name in dfh.SECTION_NAMES)
+    med = statistics.median(e2e)
+    mk = statistics.median(kern)
+    print(json.dumps({
+        "metric": "encode throughput, input GB/s (%s)" % args.workload, "unit": "GB/s",
+        "elements": int(n), "input_bytes": int(in_bytes), "containers": len(srcs),
+        "device_end_to_end_ms": round(med * 1e3, 3), "device_end_to_end_GBps": round(in_bytes / med / 1e9, 1),
+        "device_encode_kernels_ms": round(mk * 1e3, 3), "device_encode_kernels_GBps": round(in_bytes / mk / 1e9, 1),
+        "host_ms": round(t_host * 1e3, 1), "host_GBps": round(in_bytes / t_host / 1e9, 2),
+        "host_threads": os.cpu_count(), "sections_identical": bool(same), "data": "synthetic",
+        "note": "end to end = device histogram, its copy to the host, host codebook and tables, "
+                "device encode; kernels = the encode launches alone; host = compress() on all "
+                "host threads"}), flush=True)
+    if not same:
         sys.exit(1)
 
 
