@@ -455,6 +455,11 @@ void decode_kernel(const Batch batch) {
       }
     }
 
+    // The decode loops (dependent lookup chains) run at a raised wave
+    // priority, the store pass and the scan at the lowest: when waves of a
+    // SIMD compete for issue, the chains go first and the stores fill in
+    // (measured: about 1% on the BF16 block, 3% on uint8).
+    __builtin_amdgcn_s_setprio(3);
     // phase 1: count the codes that start in [gap, E).  Whole entries are
     // counted; the entry that crosses E gives back its codes that start at
     // or past E (they are the next lane's first codes).
@@ -482,6 +487,7 @@ void decode_kernel(const Batch batch) {
       rem_end = rem;
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // store the previous tile.  Its sign|mantissa registers are taken here,
     // once and on every path: the wait leaves the next step's stream words
     // in flight, and the store pass starts with no other load outstanding.
@@ -512,6 +518,7 @@ void decode_kernel(const Batch batch) {
       prev_dirty = d < out_bytes ? d : out_bytes;
     }
 
+    __builtin_amdgcn_s_setprio(3);
     // phase 2: decode again and OR the symbol bytes into the staging buffer
     // until the lane's cnt codes are written.  The entry that crosses the
     // chunk end is not clipped: its codes past the end are the next lane's
