@@ -343,6 +343,12 @@ def main():
                      "launch_ms_evented_min": round(min(launch_ms), 5)},
         "verified": verified,
     }
+    ceil = copy_ceilings(torch, dev, stream)
+    for k, v in ceil.items():
+        line["roofline"][k] = round(v, 1)
+    line["roofline"]["frac_of_copy_ceiling"] = round(achieved / max(ceil.values()), 4)
+    line["roofline"]["traffic_gbs"] = (round(traffic / (mean_ms * 1e-3) / 1e9, 1)
+                                       if traffic is not None else None)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(containers, srcs, kind)
@@ -490,6 +496,35 @@ def encode_bench(torch, dev, args):
                 "host threads"}), flush=True)
     if not same:
         sys.exit(1)
+
+
+def copy_ceilings(torch, dev, stream, mib=1024, reps=20):
+    """Read-plus-write GB/s of two plain device copies of mib MiB, each run
+    back to back between one event pair on the launch stream: the runtime's
+    device-to-device copy, and an elementwise int32 negation (a stream-copy
+    kernel: 4 bytes read and 4 written per element).  The faster of the two
+    is the practical HBM ceiling the decoder is compared with beside the
+    8 TB/s peak.  Buffers are freed on return."""
+    nbytes = mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    si, di = src.view(torch.int32), dst.view(torch.int32)
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, f in (("memcpy_d2d_gbs", lambda: dst.copy_(src)),
+                        ("stream_copy_gbs", lambda: torch.neg(si, out=di))):
+            for _ in range(3):
+                f()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                f()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            out[name] = 2 * nbytes / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9
+    del src, dst, si, di
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(torch, dev, args):

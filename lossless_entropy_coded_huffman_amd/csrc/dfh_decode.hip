@@ -57,6 +57,16 @@ constexpr int kWaitVm0 = 0x0F70;
 // staging bytes past a tile's last element that phase 2 may touch: up to four
 // lookahead symbol bytes, widened to the two words of one OR
 constexpr uint32_t kSlack = 12;
+// Table entries phase 1 keeps in registers for phase 2 to replay (a lane
+// walks about 6 entries at 2.7-bit codes); a lane with more walks the rest of
+// its chunk again from where the kept ones end.  Only the uint4 kind keeps
+// any: the BF16 kernel has no registers to spare for them (its sign|mantissa
+// prefetch holds them), and the uint8 kernel, bound by VALU issue, spends
+// on keeping and unpacking about what the replay saves (both measured).
+template <int KIND>
+constexpr uint32_t kKeep = KIND == DF_KIND_U4 ? 7u : 0u;
+template <int KIND>
+constexpr uint32_t kKeepRegs = kKeep<KIND> ? kKeep<KIND> : 1u;
 
 struct Job {
   const uint32_t *bits;  // bitstream, little-endian 32-bit words
@@ -184,6 +194,15 @@ constexpr uint32_t kOneCode = 1u << 24;
 // 32-bit code, whose length does not fit the five-bit field, drops one
 // stream word here and reports 0 bits (phase 1 takes the 32 bits off its
 // budget itself).
+// ORs an entry's symbol bytes (low word: codes 0..3, high word bits 16..23:
+// code 4) into the staging buffer at byte q.
+__device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
+  const uint64_t v = ((((uint64_t)((e.y >> 16) & 0xFFu)) << 32) | e.x) << ((q & 3) * 8);
+  lds_u32 *w = lds<lds_u32>(q & ~3u);
+  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 template <int KIND, bool CHECKED>
 __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
   const uint32_t c = long_code<CHECKED>(n_luts, t.b0, err);
@@ -465,17 +484,45 @@ void decode_kernel(const Batch batch) {
     // or past E (they are the next lane's first codes).
     uint32_t cnt = 0;
     int32_t rem_end = 0;  // E minus where the walk stopped (<= 0)
+    // the walk's first entries, for phase 2: symbol words, and the high
+    // halves of the high words (fifth symbol, code count) two to a register
+    uint32_t kept_lo[kKeepRegs<KIND>], kept_hi[(kKeepRegs<KIND> + 1) / 2];
+    Stream after = stream_at(cur.w0, cur.w1, cur.w2, gap);  // the walk past them
     {
-      Stream t = stream_at(cur.w0, cur.w1, cur.w2, gap);
+      Stream &t = after;
       int32_t rem = (int32_t)(E - gap);  // bits left before E
       uint32_t h = 0;
+      // the kept run ends at the lane's first code longer than the table's
+      // index width (kept as an entry of no codes); the loop below resumes
+      // the walk there
+      bool parked = false;
+#pragma unroll
+      for (uint32_t k = 0; k < kKeep<KIND>; k++) {
+        v2u e = {0u, 0u};
+        if (rem > 0 && !parked) {
+          e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+          if (e.y < kOneCode) {
+            e = (v2u){0u, 0u};
+            parked = true;
+          } else {
+            drop(t, e.y);
+            rem -= (int32_t)(e.y & 31);
+            cnt += e.y >> 24;
+            h = e.y;
+          }
+        }
+        kept_lo[k] = e.x;
+        if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
+        else kept_hi[k / 2] = e.y >> 16;
+      }
+      Stream t2 = t;
       while (rem > 0) {
-        h = lds<const lds_u32>(4)[(t.b0 & (kDtabEntries - 1)) << 1];
+        h = lds<const lds_u32>(4)[(t2.b0 & (kDtabEntries - 1)) << 1];
         if (h < kOneCode) {  // rare: a code longer than the table's index width
-          h = long_entry<KIND, CHECKED>(n_luts, t, batch.err).y;
+          h = long_entry<KIND, CHECKED>(n_luts, t2, batch.err).y;
           if ((h & 31) == 0) rem -= 32;
         }
-        drop(t, h);
+        drop(t2, h);
         rem -= (int32_t)(h & 31);
         cnt += h >> 24;
       }
@@ -519,8 +566,9 @@ void decode_kernel(const Batch batch) {
     }
 
     __builtin_amdgcn_s_setprio(3);
-    // phase 2: decode again and OR the symbol bytes into the staging buffer
-    // until the lane's cnt codes are written.  The entry that crosses the
+    // phase 2: walk the same entries again (those phase 1 kept are replayed
+    // from registers, the rest decoded again) and OR their symbol bytes into
+    // the staging buffer until the lane's cnt codes are written.  The entry that crosses the
     // chunk end is not clipped: its codes past the end are the next lane's
     // first codes (code boundaries are a property of the stream), written to
     // the same positions with the same values by that lane, so the OR is
@@ -536,15 +584,21 @@ void decode_kernel(const Batch batch) {
         qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
       }
-      Stream t = stream_at(cur.w0, cur.w1, cur.w2, gap);
+      // the entries phase 1 kept, in walk order, then (rare) the rest of
+      // the walk from where they end
+#pragma unroll
+      for (uint32_t k = 0; k < kKeep<KIND>; k++)
+        if (q < qend) {
+          const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
+          or_entry(q, (v2u){kept_lo[k], hi});
+          q += hi >> 24;
+        }
+      Stream t = after;
       while (q < qend) {
         v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
         if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, batch.err);  // rare
         drop(t, e.y);
-        const uint64_t v = ((((uint64_t)((e.y >> 16) & 0xFFu)) << 32) | e.x) << ((q & 3) * 8);
-        lds_u32 *w = lds<lds_u32>(q & ~3u);
-        __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        or_entry(q, e);
         q += e.y >> 24;
       }
       // uint4: a tile that ends at an odd element shares its last output
