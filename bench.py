@@ -11,8 +11,11 @@ not hold.  Prints one JSON line:
   value      decompressed BF16 GB/s = 2 n K / wall time of K steps
   roofline   algorithmic HBM bytes of one launch (stream bytes + sign|mantissa
              bytes + gap bits + tile offsets read, 2 n written) / the
-             launch's mean duration from HIP events on its stream, against
-             8 TB/s
+             launch's mean duration, against 8 TB/s.  The K launches run back
+             to back between one pair of HIP events on their stream; the mean
+             is that span over K.  Also: the same bytes against two plain
+             device copies timed in the same run, and the HBM bytes counted
+             by rocprofv3 for this kernel source (profiles/hbm_traffic.json)
   cpu_baseline  the CPU oracle's decode of the same container on the host
              cores (tile ranges on threads), a plain bit-serial reference
 
