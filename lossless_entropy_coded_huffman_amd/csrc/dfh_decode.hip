@@ -20,21 +20,27 @@
 //     4096-entry multi-code table, 32 KiB, then the hierarchical tables,
 //     512 B each), which lets two 1024-lane workgroups share a CU;
 //   - workgroups are persistent and walk the container in steps of
-//     (groups x workgroups) tiles; while a step decodes, the next step's
-//     stream words, gap fields and tile offsets are already in flight, and
-//     the current tile's sign|mantissa bytes are requested before decoding
-//     starts, so HBM latency overlaps the decode;
-//   - a lane keeps its 8 stream bytes plus the next 4 in three registers; the
-//     decode loops are split at bit 32 so that a 32-bit window is one
-//     funnel shift of a fixed register pair;
+//     (groups x workgroups) tiles, in order; the next step's stream words,
+//     gap fields and tile offsets are loaded one step ahead;
+//   - a group stores a tile one step late: the store pass of tile k shares a
+//     barrier interval with the count of tile k + 1, so HBM traffic overlaps
+//     the decode; the sign|mantissa bytes it merges are requested at the top
+//     of the step, before the count;
+//   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes)
+//     in registers and walks them as a 96-bit window shifted with funnel
+//     shifts;
 //   - a lookup in the multi-code table yields up to five codes; codes longer
 //     than 12 bits fall back to the hierarchical tables;
 //   - the per-tile prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus
 //     one LDS step across the group's four waves;
 //   - phase 2 ORs the decoded bytes into the group's LDS staging buffer,
 //     whose byte j holds output element (tile start rounded down to the
-//     store granule) + j; the store pass reads aligned LDS words, merges the
-//     sign|mantissa bytes (BF16) and issues 16-byte global stores.
+//     store granule) + j; the store pass reads aligned LDS words, clears
+//     them, merges the sign|mantissa bytes (BF16), packs nibbles (uint4) and
+//     issues 16-byte global stores, one in flight per lane (BF16);
+//   - the decode loops run at a raised wave priority, the store pass at the
+//     lowest; the uint4 kernel replays phase 1's first table entries from
+//     registers in phase 2.
 
 #include <hip/hip_runtime.h>
 
@@ -189,11 +195,6 @@ __device__ __forceinline__ void drop(Stream &t, uint32_t s) {
 // word below 2^24 marks a first code longer than the table's index width.
 constexpr uint32_t kOneCode = 1u << 24;
 
-// In place of a table entry whose first code is longer than the index width:
-// an entry for that one code (symbol byte in the low word for phase 2).  A
-// 32-bit code, whose length does not fit the five-bit field, drops one
-// stream word here and reports 0 bits (phase 1 takes the 32 bits off its
-// budget itself).
 // ORs an entry's symbol bytes (low word: codes 0..3, high word bits 16..23:
 // code 4) into the staging buffer at byte q.
 __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
@@ -203,6 +204,11 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
   __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// In place of a table entry whose first code is longer than the index width:
+// an entry for that one code (symbol byte in the low word for phase 2).  A
+// 32-bit code, whose length does not fit the five-bit field, drops one
+// stream word here and reports 0 bits (phase 1 takes the 32 bits off its
+// budget itself).
 template <int KIND, bool CHECKED>
 __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
   const uint32_t c = long_code<CHECKED>(n_luts, t.b0, err);
@@ -240,7 +246,8 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
 // each granule's exponents with its sign|mantissa bytes (the first
 // kPrefetch granules of each lane arrive in smv, the rest are loaded here).
 // A BF16 lane keeps one store in flight: it waits for the previous store
-// (s_waitcnt vmcnt(0); no load is outstanding here) before the next.  When
+// (s_waitcnt vmcnt(0), which also covers the next step's stream words,
+// requested before the count and back by then) before the next.  When
 // every wave issued its stores back to back, the write bursts delayed the
 // stream and sign|mantissa loads that the decode waits on, and the kernel
 // ran about 5% slower.
