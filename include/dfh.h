@@ -56,14 +56,21 @@
  *                  (code length << 8) | symbol; pointer = 0x8000 | table;
  *                  0xFFFF = no code.  Tables numbered breadth first.
  *                  (Digest, "Decodificacao com LUT hierarquica".)
- *   DTAB           uint64[4096], derived from lengths, not stored in files:
- *                  a decoder-side table indexed by the next 12 stream bits
- *                  that gives up to five whole codes at once.  Layout:
- *                  bits 0..31 symbol bytes of codes 0..3 (BF16: exponent
- *                  rotated right by one bit), 32..36 bits consumed, 37..47
- *                  flags for codes starting at window bits 1..11, 48..55
- *                  symbol byte of code 4, 56..63 number of codes; 0 = first
- *                  code longer than 12 bits.
+ *   DTAB           derived from lengths, not stored in files: a
+ *                  decoder-side table indexed by the next stream bits that
+ *                  gives several whole codes at once.
+ *                  BF16 and uint4: uint64[4096], indexed by 12 bits, up to
+ *                  five codes.  Layout: bits 0..31 symbol bytes of codes
+ *                  0..3 (BF16: exponent rotated right by one bit), 32..36
+ *                  bits consumed, 37..47 flags for codes starting at window
+ *                  bits 1..11, 48..55 symbol byte of code 4, 56..63 number
+ *                  of codes; 0 = first code longer than 12 bits.
+ *                  uint8: uint32[8192] indexed by 13 bits, up to two codes
+ *                  (6.6-bit codes rarely leave room for a third): bits 0..3
+ *                  bits consumed, 8..15 symbol of code 0, 16..23 symbol of
+ *                  code 1 (0 when one code), 24..31 number of codes; 0 =
+ *                  first code longer than 13 bits.  Then uint8[256]: the
+ *                  code length of each symbol.  DF_DTAB_BYTES_U8 bytes.
  * n_threads = floor(start of last code / 64) + 1 (0 when n == 0) and
  * n_tiles = ceil(n_threads / 256).
  */
@@ -106,6 +113,8 @@ typedef enum {
 #define DF_TILE_BITS 16384      /* stream bits per tile                       */
 #define DF_MAX_LUTS 64          /* cap on hierarchical tables (32 KiB)        */
 #define DF_DTAB_BITS 12         /* index width of the multi-code table        */
+#define DF_DTAB_BITS_U8 13      /* index width of the uint8 pair table        */
+#define DF_DTAB_BYTES_U8 (4 * 8192 + 256) /* uint8 DTAB: pair table + lengths */
 #define DF_MAX_BATCH 16         /* containers per df_decompress_batch launch  */
 
 /* Device error bits written by df_decompress_checked. */
@@ -257,9 +266,9 @@ df_status df_encode_layout(df_kind kind, uint64_t n, const uint64_t hist[256], u
                            const uint8_t lengths[256], df_info *out);
 
 /* The derived decode tables for these lengths: lut (room for lut_cap
- * 256-entry levels) with *n_luts levels used, and dtab (4096 entries), as in
- * the container sections LUT and DTAB.  DF_ERR_CODEBOOK when more than
- * lut_cap levels are needed. */
+ * 256-entry levels) with *n_luts levels used, and dtab (4096 words; uint8:
+ * DF_DTAB_BYTES_U8 bytes), as in the container sections LUT and DTAB.
+ * DF_ERR_CODEBOOK when more than lut_cap levels are needed. */
 df_status df_build_tables(df_kind kind, const uint8_t lengths[256], uint16_t *lut, uint32_t lut_cap,
                           uint32_t *n_luts, uint64_t *dtab);
 

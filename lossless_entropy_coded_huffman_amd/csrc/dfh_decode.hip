@@ -56,6 +56,13 @@ constexpr uint32_t kMaxGroups = 4;              // tile groups per workgroup
 constexpr uint32_t kK = DF_DTAB_BITS;           // multi-code table index width
 constexpr uint32_t kDtabEntries = 1u << kK;
 constexpr uint32_t kDtabBytes = kDtabEntries * 8;
+// uint8: the pair table (13-bit index, two codes per 32-bit entry; 6.6-bit
+// codes rarely leave room for a third) and the code length of each symbol
+constexpr uint32_t kPairMask = (1u << DF_DTAB_BITS_U8) - 1;
+constexpr uint32_t kPairLens = 4u << DF_DTAB_BITS_U8;  // LDS offset of the lengths
+// LDS bytes of a kind's decode table (the hierarchical tables follow it)
+template <int KIND>
+constexpr uint32_t kTabBytes = KIND == DF_KIND_U8 ? (uint32_t)DF_DTAB_BYTES_U8 : kDtabBytes;
 constexpr uint32_t kPrefetch = 4;  // sign|mantissa 8-byte groups requested ahead per lane
 // s_waitcnt operand (gfx9 encoding: vmcnt in bits 3..0 and 15..14, expcnt
 // in 6..4, lgkmcnt in 11..8) that waits for vmcnt 0 only
@@ -100,6 +107,7 @@ struct Batch {
 // and table offsets fold into the ds instructions' immediate fields.
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) v2u lds_v2;
@@ -112,13 +120,13 @@ __device__ __forceinline__ T *lds(uint32_t byte_offset) {
   return (T *)(uintptr_t)byte_offset;
 }
 
-// One code through the hierarchical tables (at LDS offset kDtabBytes):
+// One code through the hierarchical tables (after the kind's decode table):
 // returns (length << 8) | symbol.  A prefix with no code (possible only for
 // an incomplete code or a corrupt stream) reports DF_DEVERR_CODE in checked
 // launches and consumes one bit.
-template <bool CHECKED>
+template <int KIND, bool CHECKED>
 __device__ __forceinline__ uint32_t long_code(uint32_t n_luts, uint32_t win, uint32_t *err) {
-  const lds_u16 *lut = lds<const lds_u16>(kDtabBytes);
+  const lds_u16 *lut = lds<const lds_u16>(kTabBytes<KIND>);
   uint32_t e = lut[win & 255];
   uint32_t sh = 8;
   for (int d = 0; d < 3 && (e & 0x8000u); d++) {
@@ -211,7 +219,7 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
 // budget itself).
 template <int KIND, bool CHECKED>
 __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
-  const uint32_t c = long_code<CHECKED>(n_luts, t.b0, err);
+  const uint32_t c = long_code<KIND, CHECKED>(n_luts, t.b0, err);
   uint32_t len = c >> 8;
   if (len >= 32) {
     t.b0 = t.b1;
@@ -220,6 +228,7 @@ __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *
     len = 0;
   }
   const uint32_t sym = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+  if (KIND == DF_KIND_U8) return (v2u){0u, kOneCode | (sym << 8) | len};  // a pair-table entry
   return (v2u){sym, kOneCode | len};
 }
 
@@ -380,28 +389,29 @@ void decode_kernel(const Batch batch) {
   const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
   const uint32_t out_bytes = batch.out_bytes;
-  const uint32_t buf = kDtabBytes + batch.lut_bytes + grp * out_bytes;  // LDS byte offset
-  lds_u32 *wsum = lds<lds_u32>(kDtabBytes + batch.lut_bytes + groups * out_bytes);
+  const uint32_t buf = kTabBytes<KIND> + batch.lut_bytes + grp * out_bytes;  // LDS byte offset
+  lds_u32 *wsum = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes);
 
   {  // stage the tables once per workgroup: the first four 16-byte words per
      // lane (all a 1024-lane workgroup needs for up to 64 levels) with every
      // load issued before any write, the rest one by one
-    const uint32_t total = kDtabBytes / 16 + n_luts * 32;  // 16-byte words: table, then levels
+    constexpr uint32_t kTabWords = kTabBytes<KIND> / 16;
+    const uint32_t total = kTabWords + n_luts * 32;  // 16-byte words: table, then levels
     const v4u *dsrc = (const v4u *)jb.dtab;
-    const v4u *lsrc = (const v4u *)jb.lut - kDtabBytes / 16;
+    const v4u *lsrc = (const v4u *)jb.lut - kTabWords;
     lds_v4 *dl = lds<lds_v4>(0);
     const uint32_t i0 = tid, i1 = tid + blockDim.x, i2 = tid + 2 * blockDim.x, i3 = tid + 3 * blockDim.x;
     const v4u z = {0u, 0u, 0u, 0u};
-    const v4u t0 = i0 < total ? (i0 < kDtabBytes / 16 ? dsrc[i0] : lsrc[i0]) : z;
-    const v4u t1 = i1 < total ? (i1 < kDtabBytes / 16 ? dsrc[i1] : lsrc[i1]) : z;
-    const v4u t2 = i2 < total ? (i2 < kDtabBytes / 16 ? dsrc[i2] : lsrc[i2]) : z;
-    const v4u t3 = i3 < total ? (i3 < kDtabBytes / 16 ? dsrc[i3] : lsrc[i3]) : z;
+    const v4u t0 = i0 < total ? (i0 < kTabWords ? dsrc[i0] : lsrc[i0]) : z;
+    const v4u t1 = i1 < total ? (i1 < kTabWords ? dsrc[i1] : lsrc[i1]) : z;
+    const v4u t2 = i2 < total ? (i2 < kTabWords ? dsrc[i2] : lsrc[i2]) : z;
+    const v4u t3 = i3 < total ? (i3 < kTabWords ? dsrc[i3] : lsrc[i3]) : z;
     if (i0 < total) dl[i0] = t0;
     if (i1 < total) dl[i1] = t1;
     if (i2 < total) dl[i2] = t2;
     if (i3 < total) dl[i3] = t3;
     for (uint32_t i = tid + 4 * blockDim.x; i < total; i += blockDim.x)
-      dl[i] = i < kDtabBytes / 16 ? dsrc[i] : lsrc[i];
+      dl[i] = i < kTabWords ? dsrc[i] : lsrc[i];
   }
 
   const uint64_t step = (uint64_t)jb.wg_count * groups;
@@ -524,7 +534,8 @@ void decode_kernel(const Batch batch) {
       }
       Stream t2 = t;
       while (rem > 0) {
-        h = lds<const lds_u32>(4)[(t2.b0 & (kDtabEntries - 1)) << 1];
+        h = KIND == DF_KIND_U8 ? lds<const lds_u32>(0)[t2.b0 & kPairMask]
+                               : lds<const lds_u32>(4)[(t2.b0 & (kDtabEntries - 1)) << 1];
         if (h < kOneCode) {  // rare: a code longer than the table's index width
           h = long_entry<KIND, CHECKED>(n_luts, t2, batch.err).y;
           if ((h & 31) == 0) rem -= 32;
@@ -534,9 +545,14 @@ void decode_kernel(const Batch batch) {
         cnt += h >> 24;
       }
       if (rem < 0) {
-        // bits of the last entry before E (1..11; a one-code entry has no flags)
+        // bits of the last entry before E (1..12; a one-code entry has no flags)
         const uint32_t r = (uint32_t)(rem + (int32_t)(h & 31));
-        cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
+        if (KIND == DF_KIND_U8) {
+          // a pair: the second code starts at (consumed - its length)
+          if ((h >> 24) == 2 && (h & 31) - lds<const lds_u8>(kPairLens)[(h >> 16) & 0xFFu] >= r) cnt -= 1;
+        } else {
+          cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
+        }
       }
       rem_end = rem;
     }
@@ -601,12 +617,26 @@ void decode_kernel(const Batch batch) {
           q += hi >> 24;
         }
       Stream t = after;
-      while (q < qend) {
-        v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
-        if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, batch.err);  // rare
-        drop(t, e.y);
-        or_entry(q, e);
-        q += e.y >> 24;
+      if (KIND == DF_KIND_U8) {
+        while (q < qend) {
+          uint32_t h = lds<const lds_u32>(0)[t.b0 & kPairMask];
+          if (h < kOneCode) h = long_entry<KIND, CHECKED>(n_luts, t, batch.err).y;  // rare
+          drop(t, h);
+          // symbol bytes of the pair (bits 8..23) at q
+          const uint64_t v = (uint64_t)__builtin_amdgcn_ubfe(h, 8, 16) << ((q & 3) * 8);
+          lds_u32 *w = lds<lds_u32>(q & ~3u);
+          __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          q += h >> 24;
+        }
+      } else {
+        while (q < qend) {
+          v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+          if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, batch.err);  // rare
+          drop(t, e.y);
+          or_entry(q, e);
+          q += e.y >> 24;
+        }
       }
       // uint4: a tile that ends at an odd element shares its last output
       // byte with the next tile, and writes that whole byte, so it needs the
@@ -622,7 +652,7 @@ void decode_kernel(const Batch batch) {
         const uint32_t win = p >= 64 ? __builtin_amdgcn_alignbit(cur.w3, cur.w2, p - 64)
                            : p >= 32 ? __builtin_amdgcn_alignbit(cur.w2, cur.w1, p - 32)
                                      : __builtin_amdgcn_alignbit(cur.w1, cur.w0, p);
-        const uint32_t c = long_code<CHECKED>(n_luts, win, batch.err);
+        const uint32_t c = long_code<KIND, CHECKED>(n_luts, win, batch.err);
         __hip_atomic_fetch_or(lds<lds_u32>(q & ~3u), (c & 0xFFu) << ((q & 3) * 8), __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_WORKGROUP);
       }
@@ -753,7 +783,8 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     int per_cu = 0;
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
-      const size_t need = (size_t)kDtabBytes + lut_bytes + (size_t)g * out_bytes + 16 * g;
+      const size_t need = (size_t)(kind == DF_KIND_U8 ? kTabBytes<DF_KIND_U8> : kDtabBytes) + lut_bytes +
+                          (size_t)g * out_bytes + 16 * g;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=

@@ -263,10 +263,38 @@ int build_tables(const uint8_t *len, std::vector<uint16_t> &lut) {
   return (int)tabs.size();
 }
 
+// One code through the hierarchical tables from the low bits of look:
+// (length << 8) | symbol, or 0 when no code ends within 16 bits.
+uint32_t lut_code(const std::vector<uint16_t> &lut, uint32_t look) {
+  uint16_t e = lut[look & 255];
+  if (e != 0xFFFF && (e & 0x8000)) e = lut[(size_t)(e & 0x7FFF) * 256 + ((look >> 8) & 255)];
+  return (e == 0xFFFF || (e & 0x8000)) ? 0u : e;
+}
+
+// uint8 pair table: entry w holds the whole codes inside the 13-bit window
+// w, at most two, then the code length of every symbol.  Layout in
+// include/dfh.h (section DTAB).
+void build_pair_table(const uint8_t lengths[256], const std::vector<uint16_t> &lut, std::vector<uint8_t> &out) {
+  out.assign(DF_DTAB_BYTES_U8, 0);
+  for (uint32_t w = 0; w < (1u << DF_DTAB_BITS_U8); w++) {
+    uint32_t pos = 0, count = 0, syms = 0;
+    while (count < 2 && pos < (uint32_t)DF_DTAB_BITS_U8) {
+      const uint32_t e = lut_code(lut, w >> pos);
+      if (!e || pos + (e >> 8) > (uint32_t)DF_DTAB_BITS_U8) break;
+      syms |= (e & 0xFF) << (8 * count);
+      pos += e >> 8;
+      count++;
+    }
+    const uint32_t v = count ? pos | (syms << 8) | (count << 24) : 0u;
+    memcpy(&out[4 * (size_t)w], &v, 4);
+  }
+  memcpy(&out[(size_t)4 << DF_DTAB_BITS_U8], lengths, 256);
+}
+
 // Multi-code decode table: entry w lists the whole codes inside the 12-bit
 // window w (first stream bit = bit 0), at most five, found by walking the
 // hierarchical tables.  Layout in include/dfh.h (section DTAB).
-void build_dtab(df_kind kind, const std::vector<uint16_t> &lut, std::vector<uint64_t> &dtab) {
+void build_multi_table(df_kind kind, const std::vector<uint16_t> &lut, std::vector<uint64_t> &dtab) {
   dtab.assign(kDtabSize, 0);
   for (uint32_t w = 0; w < (uint32_t)kDtabSize; w++) {
     uint64_t syms = 0, starts = 0;
@@ -290,6 +318,23 @@ void build_dtab(df_kind kind, const std::vector<uint16_t> &lut, std::vector<uint
       dtab[w] = (syms & 0xFFFFFFFFull) | ((uint64_t)pos << 32) | ((starts >> 1) << 37) | ((syms >> 32) << 48) |
                 ((uint64_t)count << 56);
   }
+}
+
+uint64_t dtab_bytes(df_kind kind) {
+  return kind == DF_KIND_U8 ? DF_DTAB_BYTES_U8 : (uint64_t)kDtabSize * 8;
+}
+
+// The DTAB section of a kind (bytes).
+void build_dtab(df_kind kind, const uint8_t lengths[256], const std::vector<uint16_t> &lut,
+                std::vector<uint8_t> &out) {
+  if (kind == DF_KIND_U8) {
+    build_pair_table(lengths, lut, out);
+    return;
+  }
+  std::vector<uint64_t> t;
+  build_multi_table(kind, lut, t);
+  out.resize(t.size() * 8);
+  memcpy(out.data(), t.data(), out.size());
 }
 
 }  // namespace
@@ -323,10 +368,10 @@ df_status finish_tables(df_container *c) {
   c->info.n_luts = (uint32_t)nl;
   if (!c->alloc(DF_SEC_LUT, lut.size() * 2)) return DF_ERR_ALLOC;
   memcpy(c->sec[DF_SEC_LUT], lut.data(), lut.size() * 2);
-  std::vector<uint64_t> dtab;
-  build_dtab(c->info.kind, lut, dtab);
-  if (!c->alloc(DF_SEC_DTAB, dtab.size() * 8)) return DF_ERR_ALLOC;
-  memcpy(c->sec[DF_SEC_DTAB], dtab.data(), dtab.size() * 8);
+  std::vector<uint8_t> dtab;
+  build_dtab(c->info.kind, c->info.lengths, lut, dtab);
+  if (!c->alloc(DF_SEC_DTAB, dtab.size())) return DF_ERR_ALLOC;
+  memcpy(c->sec[DF_SEC_DTAB], dtab.data(), dtab.size());
   return DF_OK;
 }
 
@@ -539,7 +584,7 @@ df_status df_encode_layout(df_kind kind, uint64_t n, const uint64_t hist[256], u
   in.section_bytes[DF_SEC_TILE_OUT] = (in.n_tiles + 1) * 8;
   in.section_bytes[DF_SEC_SIGN_MANTISSA] = kind == DF_KIND_BF16 ? round_up(n, 64) : 0;
   in.section_bytes[DF_SEC_LUT] = lut.size() * 2;
-  in.section_bytes[DF_SEC_DTAB] = (uint64_t)kDtabSize * 8;
+  in.section_bytes[DF_SEC_DTAB] = dtab_bytes(kind);
   *out = in;
   return DF_OK;
 }
@@ -552,9 +597,9 @@ df_status df_build_tables(df_kind kind, const uint8_t lengths[256], uint16_t *lu
   if (nl < 0 || (uint32_t)nl > lut_cap) return DF_ERR_CODEBOOK;
   memcpy(lut, l.data(), l.size() * 2);
   *n_luts = (uint32_t)nl;
-  std::vector<uint64_t> d;
-  build_dtab(kind, l, d);
-  memcpy(dtab, d.data(), d.size() * 8);
+  std::vector<uint8_t> d;
+  build_dtab(kind, lengths, l, d);
+  memcpy(dtab, d.data(), d.size());
   return DF_OK;
 }
 
@@ -593,8 +638,7 @@ df_status df_container_validate(const df_container *c) {
   if (in.total_bits < in.n || in.total_bits > in.n * DF_MAX_LEN) return DF_ERR_FORMAT;
   const uint64_t want[DF_SEC_COUNT] = {
       in.n_tiles * (DF_TILE_BITS / 8) + 16, in.n_tiles * kGapBytesPerTile + 16, (in.n_tiles + 1) * 8,
-      in.kind == DF_KIND_BF16 ? round_up(in.n, 64) : 0, (uint64_t)in.n_luts * 512,
-      (uint64_t)kDtabSize * 8};
+      in.kind == DF_KIND_BF16 ? round_up(in.n, 64) : 0, (uint64_t)in.n_luts * 512, dtab_bytes(in.kind)};
   for (int s = 0; s < DF_SEC_COUNT; s++)
     if (in.section_bytes[s] != want[s] || !c->sec[s]) return DF_ERR_FORMAT;
   const uint64_t *to = (const uint64_t *)c->sec[DF_SEC_TILE_OUT];
@@ -616,9 +660,9 @@ df_status df_container_validate(const df_container *c) {
   int nl = build_tables(in.lengths, lut);
   if (nl < 0 || (uint32_t)nl != in.n_luts || memcmp(lut.data(), c->sec[DF_SEC_LUT], lut.size() * 2))
     return DF_ERR_CORRUPT;
-  std::vector<uint64_t> dtab;
-  build_dtab(in.kind, lut, dtab);
-  if (memcmp(dtab.data(), c->sec[DF_SEC_DTAB], dtab.size() * 8)) return DF_ERR_CORRUPT;
+  std::vector<uint8_t> dtab;
+  build_dtab(in.kind, in.lengths, lut, dtab);
+  if (memcmp(dtab.data(), c->sec[DF_SEC_DTAB], dtab.size())) return DF_ERR_CORRUPT;
   return DF_OK;
 }
 
@@ -700,10 +744,10 @@ df_status df_container_load(const char *path, df_container **out) {
     std::vector<uint16_t> lut;
     if (build_tables(c->info.lengths, lut) < 0) st = DF_ERR_CORRUPT;
     else {
-      std::vector<uint64_t> dtab;
-      build_dtab(c->info.kind, lut, dtab);
-      if (!c->alloc(DF_SEC_DTAB, dtab.size() * 8)) st = DF_ERR_ALLOC;
-      else memcpy(c->sec[DF_SEC_DTAB], dtab.data(), dtab.size() * 8);
+      std::vector<uint8_t> dtab;
+      build_dtab(c->info.kind, c->info.lengths, lut, dtab);
+      if (!c->alloc(DF_SEC_DTAB, dtab.size())) st = DF_ERR_ALLOC;
+      else memcpy(c->sec[DF_SEC_DTAB], dtab.data(), dtab.size());
     }
   }
   if (st == DF_OK) st = df_container_validate(c);

@@ -368,11 +368,16 @@ def df_encode_layout(kind: int, n: int, hist, last_symbol: int, lengths) -> df_i
     return out
 
 
+DTAB_BYTES_U8 = 4 * 8192 + 256   # uint8: pair table, then the code lengths
+DTAB_BYTES = 8 * 4096             # BF16 and uint4: multi-code table
+
+
 def df_build_tables(kind: int, lengths, lut_cap: int = 64):
-    """(lut uint16[n_luts * 256], n_luts, dtab uint64[4096])."""
+    """(lut uint16[n_luts * 256], n_luts, dtab as uint64 words: the DTAB
+    section's bytes)."""
     ln = np.ascontiguousarray(lengths, np.uint8)
     lut = np.zeros(lut_cap * 256, np.uint16)
-    dtab = np.zeros(1 << 12, np.uint64)
+    dtab = np.zeros((DTAB_BYTES_U8 if kind == KIND_U8 else DTAB_BYTES) // 8, np.uint64)
     nl = ctypes.c_uint32(0)
     _check(lib().df_build_tables(kind, ln.ctypes.data, lut.ctypes.data, int(lut_cap), ctypes.byref(nl),
                                  dtab.ctypes.data), "df_build_tables")
