@@ -39,8 +39,8 @@
 //     them, merges the sign|mantissa bytes (BF16), packs nibbles (uint4) and
 //     issues 16-byte global stores, one in flight per lane (BF16);
 //   - the decode loops run at a raised wave priority, the store pass at the
-//     lowest; the uint4 kernel replays phase 1's first table entries from
-//     registers in phase 2.
+//     lowest; the uint4 and uint8 kernels replay phase 1's first table
+//     entries from registers in phase 2.
 
 #include <hip/hip_runtime.h>
 
@@ -70,14 +70,14 @@ constexpr int kWaitVm0 = 0x0F70;
 // staging bytes past a tile's last element that phase 2 may touch: up to four
 // lookahead symbol bytes, widened to the two words of one OR
 constexpr uint32_t kSlack = 12;
-// Table entries phase 1 keeps in registers for phase 2 to replay (a lane
-// walks about 6 entries at 2.7-bit codes); a lane with more walks the rest of
-// its chunk again from where the kept ones end.  Only the uint4 kind keeps
-// any: the BF16 kernel has no registers to spare for them (its sign|mantissa
-// prefetch holds them), and the uint8 kernel, bound by VALU issue, spends
-// on keeping and unpacking about what the replay saves (both measured).
+// Table entries phase 1 keeps in registers for phase 2 to replay; a lane
+// with more walks the rest of its chunk again from where the kept ones end.
+// Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
+// 2.7-bit codes), uint8 4 of its pair-table words (every unrolled step costs
+// the whole wave, and the uint8 kernel is bound by VALU issue), BF16 none
+// (its sign|mantissa prefetch holds the registers they would need).
 template <int KIND>
-constexpr uint32_t kKeep = KIND == DF_KIND_U4 ? 7u : 0u;
+constexpr uint32_t kKeep = KIND == DF_KIND_U4 ? 7u : KIND == DF_KIND_U8 ? 4u : 0u;
 template <int KIND>
 constexpr uint32_t kKeepRegs = kKeep<KIND> ? kKeep<KIND> : 1u;
 
@@ -217,6 +217,15 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
 // 32-bit code, whose length does not fit the five-bit field, drops one
 // stream word here and reports 0 bits (phase 1 takes the 32 bits off its
 // budget itself).
+// ORs a pair-table entry's symbol bytes (bits 8..23) into the staging
+// buffer at byte q.
+__device__ __forceinline__ void or_pair(uint32_t q, uint32_t h) {
+  const uint64_t v = (uint64_t)__builtin_amdgcn_ubfe(h, 8, 16) << ((q & 3) * 8);
+  lds_u32 *w = lds<lds_u32>(q & ~3u);
+  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 template <int KIND, bool CHECKED>
 __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
   const uint32_t c = long_code<KIND, CHECKED>(n_luts, t.b0, err);
@@ -517,7 +526,8 @@ void decode_kernel(const Batch batch) {
       for (uint32_t k = 0; k < kKeep<KIND>; k++) {
         v2u e = {0u, 0u};
         if (rem > 0 && !parked) {
-          e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+          if (KIND == DF_KIND_U8) e.y = lds<const lds_u32>(0)[t.b0 & kPairMask];
+          else e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
           if (e.y < kOneCode) {
             e = (v2u){0u, 0u};
             parked = true;
@@ -528,9 +538,13 @@ void decode_kernel(const Batch batch) {
             h = e.y;
           }
         }
-        kept_lo[k] = e.x;
-        if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
-        else kept_hi[k / 2] = e.y >> 16;
+        if (KIND == DF_KIND_U8) {  // a pair-table entry is one word
+          kept_lo[k] = e.y;
+        } else {
+          kept_lo[k] = e.x;
+          if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
+          else kept_hi[k / 2] = e.y >> 16;
+        }
       }
       Stream t2 = t;
       while (rem > 0) {
@@ -612,9 +626,14 @@ void decode_kernel(const Batch batch) {
 #pragma unroll
       for (uint32_t k = 0; k < kKeep<KIND>; k++)
         if (q < qend) {
-          const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
-          or_entry(q, (v2u){kept_lo[k], hi});
-          q += hi >> 24;
+          if (KIND == DF_KIND_U8) {
+            or_pair(q, kept_lo[k]);
+            q += kept_lo[k] >> 24;
+          } else {
+            const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
+            or_entry(q, (v2u){kept_lo[k], hi});
+            q += hi >> 24;
+          }
         }
       Stream t = after;
       if (KIND == DF_KIND_U8) {
@@ -622,11 +641,7 @@ void decode_kernel(const Batch batch) {
           uint32_t h = lds<const lds_u32>(0)[t.b0 & kPairMask];
           if (h < kOneCode) h = long_entry<KIND, CHECKED>(n_luts, t, batch.err).y;  // rare
           drop(t, h);
-          // symbol bytes of the pair (bits 8..23) at q
-          const uint64_t v = (uint64_t)__builtin_amdgcn_ubfe(h, 8, 16) << ((q & 3) * 8);
-          lds_u32 *w = lds<lds_u32>(q & ~3u);
-          __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          or_pair(q, h);
           q += h >> 24;
         }
       } else {
