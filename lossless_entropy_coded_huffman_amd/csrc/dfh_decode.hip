@@ -336,7 +336,9 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
         o.z &= wk == 2 ? m : ~0u;
         o.w &= wk == 3 ? m : ~0u;
       }
-      if (b0 >= blo && b0 + 16 <= bhi) *(v4u *)(dst_t + b0) = (v4u){o.x, o.y, o.z, o.w};
+      // non-temporal: 2.4% faster on the uint4 block (BF16 measured 1.4%
+      // slower, uint8 the same)
+      if (b0 >= blo && b0 + 16 <= bhi) __builtin_nontemporal_store((v4u){o.x, o.y, o.z, o.w}, (v4u *)(dst_t + b0));
       else store_partial(dst_t, b0, blo, bhi, o);
     }
   } else {
