@@ -220,7 +220,15 @@ typedef struct {
  * on-chip memory.  One launch covers the whole container (the digest's
  * "Descompressao por bloco de transformer": one batch per block).
  * n == 0 enqueues nothing.  DF_ERR_ARG on bad pointers, kind, alignment,
- * or sizes; DF_ERR_HIP when the launch fails. */
+ * or sizes; DF_ERR_HIP when the launch fails.
+ * Scheduling: a BF16 container of more than three steps of tiles (three
+ * times the launch's tile groups) is decoded with tiles handed out by
+ * device-side counters that the library keeps in its code object (no
+ * allocation; each launch leaves its counters zero).  Up to 3584 such jobs
+ * may be in flight on one device at once; a launch under stream capture
+ * takes one of 512 counter slots reserved for graphs for the life of the
+ * process, after which captured launches use the static tile order.  The
+ * decoded bytes do not depend on the schedule. */
 df_status df_decompress(const df_device_view *v, void *dst, hipStream_t stream);
 
 /* As df_decompress, and also checks every tile on the device: d_err (one
