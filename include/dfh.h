@@ -260,8 +260,9 @@ df_status df_decompress_batch(const df_device_view *views, void *const *dsts, ui
  * Device calls enqueue on the stream and return, as for decompression. */
 
 /* Histogram of the coded symbols of n device elements (layout as for
- * df_histogram) into d_hist, 256 device uint64 counts; the call clears them
- * first.  DF_ERR_ARG on a null pointer or bad kind. */
+ * df_histogram; d_src 16-byte aligned) into d_hist, 256 device uint64
+ * counts; the call clears them first.  DF_ERR_ARG on a null or misaligned
+ * pointer or a bad kind. */
 df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint64_t *d_hist,
                               hipStream_t stream);
 
@@ -283,8 +284,8 @@ df_status df_build_tables(df_kind kind, const uint8_t lengths[256], uint16_t *lu
 /* Device workspace bytes df_encode_device needs for n elements. */
 uint64_t df_encode_workspace_bytes(uint64_t n);
 
-/* Encode n device elements into device sections sized by df_encode_layout
- * (layout is its result): bitstream, gaps, tile_out and, for BF16,
+/* Encode n device elements (d_src 16-byte aligned) into device sections
+ * sized by df_encode_layout (layout is its result): bitstream, gaps, tile_out and, for BF16,
  * sign_mantissa (NULL otherwise).  d_workspace: df_encode_workspace_bytes(n)
  * bytes, 16-byte aligned.  d_max_tile (one device uint32) receives
  * max_tile_elems.  Each element's code goes at the sum of the lengths of

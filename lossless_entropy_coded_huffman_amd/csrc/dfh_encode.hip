@@ -12,7 +12,7 @@
 // Each element's code starts at the sum of the lengths of the codes before
 // it.  That sum is a scan over the elements, done in three launches:
 //   enc_sums   one workgroup per block of kBlock elements sums its lengths;
-//   enc_scan   one workgroup turns the block sums into block start bits;
+//   enc_scan_local, enc_scan_add   the block sums into block start bits;
 //   enc_write  each workgroup rescans its block, packs its codes into an
 //              LDS bit buffer and writes it out (interior words with plain
 //              stores; the first and last words, shared with the
@@ -45,21 +45,82 @@ __device__ __forceinline__ uint32_t symbol_at(int kind, const void *src, uint64_
   return ((const uint8_t *)src)[i];
 }
 
+// The raw bytes of elements i0 .. i0 + kPerThread - 1 (all below n), with
+// 16-byte loads (i0 is a multiple of kPerThread, so they are aligned): 32
+// bytes for BF16, 16 for uint8, 8 for uint4.
+__device__ __forceinline__ void load16(int kind, const void *src, uint64_t i0, uint4 &a, uint4 &b) {
+  if (kind == DF_KIND_BF16) {
+    const uint4 *p = (const uint4 *)((const uint16_t *)src + i0);
+    a = p[0];
+    b = p[1];
+  } else if (kind == DF_KIND_U8) {
+    a = *(const uint4 *)((const uint8_t *)src + i0);
+  } else {
+    const uint2 v = *(const uint2 *)((const uint8_t *)src + i0 / 2);
+    a = make_uint4(v.x, v.y, 0u, 0u);
+  }
+}
+
+// Their symbols.
+__device__ __forceinline__ void extract16(int kind, const uint4 &a, const uint4 &b, uint32_t (&s)[kPerThread]) {
+  if (kind == DF_KIND_BF16) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (uint32_t k = 0; k < 8; k++) {
+      s[2 * k] = (w[k] >> 7) & 0xFFu;
+      s[2 * k + 1] = (w[k] >> 23) & 0xFFu;
+    }
+  } else if (kind == DF_KIND_U8) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (uint32_t k = 0; k < 16; k++) s[k] = (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+  } else {
+    const uint32_t w[2] = {a.x, a.y};
+#pragma unroll
+    for (uint32_t k = 0; k < 16; k++) s[k] = (w[k >> 3] >> (4 * (k & 7))) & 0xFu;
+  }
+}
+
+__device__ __forceinline__ void symbols16(int kind, const void *src, uint64_t i0, uint32_t (&s)[kPerThread]) {
+  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+  load16(kind, src, i0, a, b);
+  extract16(kind, a, b, s);
+}
+
 __global__ void fill_zero(uint32_t *p, uint64_t words) {
   for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
        i += (uint64_t)gridDim.x * blockDim.x)
     p[i] = 0;
 }
 
+// Sixteen 256-bin LDS histograms per workgroup, four per wave chosen by
+// lane, so few lanes add to one bin at a time (coded symbols crowd into a
+// few bins); each padded to 257 words so that one bin of different copies
+// sits in different banks.  16 consecutive elements per thread per step.
+constexpr uint32_t kSubHists = 16, kSubStride = 257;
 __global__ __launch_bounds__(kThreads) void histogram_kernel(int kind, const void *src, uint64_t n,
                                                              unsigned long long *hist) {
-  __shared__ uint32_t h[256];
-  h[threadIdx.x] = 0;
+  __shared__ uint32_t h[kSubHists * kSubStride];
+  for (uint32_t k = threadIdx.x; k < kSubHists * kSubStride; k += kThreads) h[k] = 0;
   __syncthreads();
-  for (uint64_t i = blockIdx.x * (uint64_t)kThreads + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kThreads)
-    atomicAdd(&h[symbol_at(kind, src, i)], 1u);
+  uint32_t *hw = h + ((threadIdx.x >> 6) * 4 + (threadIdx.x & 3)) * kSubStride;
+  const uint64_t chunks = (n + kPerThread - 1) / kPerThread;
+  for (uint64_t c = blockIdx.x * (uint64_t)kThreads + threadIdx.x; c < chunks; c += (uint64_t)gridDim.x * kThreads) {
+    const uint64_t i0 = c * kPerThread;
+    if (i0 + kPerThread <= n) {
+      uint32_t sy[kPerThread];
+      symbols16(kind, src, i0, sy);
+#pragma unroll
+      for (uint32_t k = 0; k < kPerThread; k++) atomicAdd(&hw[sy[k]], 1u);
+    } else {
+      for (uint64_t i = i0; i < n; i++) atomicAdd(&hw[symbol_at(kind, src, i)], 1u);
+    }
+  }
   __syncthreads();
-  if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], (unsigned long long)h[threadIdx.x]);
+  uint32_t t = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < kSubHists; j++) t += h[j * kSubStride + threadIdx.x];
+  if (t) atomicAdd(&hist[threadIdx.x], (unsigned long long)t);
 }
 
 // Sum of the workgroup's 256 values, returned to every thread.
@@ -94,41 +155,54 @@ __global__ __launch_bounds__(kThreads) void enc_sums(int kind, const void *src, 
   __shared__ uint32_t scratch[4];
   len[threadIdx.x] = cb.len[threadIdx.x];
   __syncthreads();
-  const uint64_t b0 = (uint64_t)blockIdx.x * kBlock;
+  const uint64_t i0 = (uint64_t)blockIdx.x * kBlock + (uint64_t)threadIdx.x * kPerThread;
   uint32_t s = 0;
-  for (uint32_t k = 0; k < kPerThread; k++) {
-    const uint64_t i = b0 + (uint64_t)k * kThreads + threadIdx.x;
-    if (i < n) s += len[symbol_at(kind, src, i)];
+  if (i0 + kPerThread <= n) {
+    uint32_t sy[kPerThread];
+    symbols16(kind, src, i0, sy);
+#pragma unroll
+    for (uint32_t k = 0; k < kPerThread; k++) s += len[sy[k]];
+  } else {
+    for (uint64_t i = i0; i < n; i++) s += len[symbol_at(kind, src, i)];
   }
   s = block_sum(s, scratch);
   if (threadIdx.x == 0) block_sums[blockIdx.x] = s;
 }
 
-// One workgroup: block_base[b] = sum of block_sums[0 .. b).
-__global__ __launch_bounds__(1024) void enc_scan(const uint64_t *block_sums, uint64_t nblocks,
-                                                 uint64_t *block_base) {
-  __shared__ uint64_t part[1024];
-  const uint64_t per = (nblocks + 1023) / 1024;
-  const uint64_t b = threadIdx.x * per, e = b + per < nblocks ? b + per : nblocks;
-  uint64_t s = 0;
-  for (uint64_t i = b; i < e; i++) s += block_sums[i];
-  part[threadIdx.x] = s;
+// block_base[b] = sum of block_sums[0 .. b), in two launches over
+// segments of 1024 blocks: enc_scan_local scans each segment (coalesced) and
+// records its total; enc_scan_add adds the totals of the segments before.
+__global__ __launch_bounds__(1024) void enc_scan_local(const uint64_t *block_sums, uint64_t nblocks,
+                                                       uint64_t *block_base, uint64_t *seg_total) {
+  __shared__ uint64_t part[16];
+  const uint64_t i = blockIdx.x * 1024ull + threadIdx.x;
+  const uint64_t v = i < nblocks ? block_sums[i] : 0;
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t x = v;  // inclusive within the wave
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o);
+    if (lane >= (uint32_t)o) x += y;
+  }
+  if (lane == 63) part[wv] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {  // 1024 partial sums, sequentially
-    uint64_t run = 0;
-    for (int t = 0; t < 1024; t++) {
-      const uint64_t v = part[t];
-      part[t] = run;
-      run += v;
-    }
+  uint64_t before = 0;
+  for (uint32_t k = 0; k < wv; k++) before += part[k];
+  if (i < nblocks) block_base[i] = before + x - v;
+  if (threadIdx.x == 1023) seg_total[blockIdx.x] = before + x;
+}
+
+__global__ __launch_bounds__(1024) void enc_scan_add(uint64_t *block_base, uint64_t nblocks,
+                                                     const uint64_t *seg_total) {
+  __shared__ uint64_t pre;
+  if (threadIdx.x < 64) {
+    uint64_t t = 0;
+    for (uint32_t k = threadIdx.x; k < blockIdx.x; k += 64) t += seg_total[k];
+    for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+    if (threadIdx.x == 0) pre = t;
   }
   __syncthreads();
-  uint64_t run = part[threadIdx.x];
-  for (uint64_t i = b; i < e; i++) {
-    const uint64_t v = block_sums[i];
-    block_base[i] = run;
-    run += v;
-  }
+  const uint64_t i = blockIdx.x * 1024ull + threadIdx.x;
+  if (i < nblocks) block_base[i] += pre;
 }
 
 __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src, uint64_t n, Codebook cb,
@@ -140,62 +214,93 @@ __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src,
   // the block's codes, from the word its first bit falls in: at most
   // kBlock * 32 bits starting up to 31 bits into word 0, so words 0..kBlock
   __shared__ uint32_t buf[kBlock + 1];
+  // the gap fields of the chunks whose first code is in this block, from
+  // the gap word of the block's first chunk: at most kBlock * 32 / 64
+  // chunks plus the partial ones at both ends
+  constexpr uint32_t kGapWords = ((kBlock * 32 / 64 + 2) * kGapBits) / 32 + 4;
+  __shared__ uint32_t gbuf[kGapWords];
+  // the element loads, the block's first bit and the element before this
+  // thread's first go in flight first, so their latency overlaps the
+  // codebook staging below
+  const uint64_t b0 = (uint64_t)blockIdx.x * kBlock;
+  const uint64_t i0 = b0 + (uint64_t)threadIdx.x * kPerThread;  // this thread's first element
+  const bool full = i0 + kPerThread <= n;
+  uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = ra;
+  if (full) load16(kind, src, i0, ra, rb);
+  const uint64_t base = block_base[blockIdx.x];
+  const uint32_t prev_sym = i0 > 0 && i0 < n ? symbol_at(kind, src, i0 - 1) : 0u;
   rev[threadIdx.x] = cb.rev[threadIdx.x];
   len[threadIdx.x] = cb.len[threadIdx.x];
   for (uint32_t k = threadIdx.x; k < kBlock + 1; k += kThreads) buf[k] = 0;
+  for (uint32_t k = threadIdx.x; k < kGapWords; k += kThreads) gbuf[k] = 0;
   __syncthreads();
 
-  const uint64_t b0 = (uint64_t)blockIdx.x * kBlock;
-  const uint64_t i0 = b0 + (uint64_t)threadIdx.x * kPerThread;  // this thread's first element
   uint32_t syms[kPerThread];
   uint32_t mine = 0;
+  if (full) {
+    extract16(kind, ra, rb, syms);
+  } else {
 #pragma unroll
-  for (uint32_t k = 0; k < kPerThread; k++) {
-    syms[k] = i0 + k < n ? symbol_at(kind, src, i0 + k) : 0u;
-    mine += i0 + k < n ? len[syms[k]] : 0u;
+    for (uint32_t k = 0; k < kPerThread; k++) syms[k] = i0 + k < n ? symbol_at(kind, src, i0 + k) : 0u;
   }
-  const uint64_t base = block_base[blockIdx.x];
-  const uint64_t word0 = base >> 5;  // global word of the block's first bit
-  uint64_t pos = base + block_exclusive(mine, scratch);
-  // start of the element before this thread's first one
-  uint64_t prev = 0;
-  if (i0 > 0 && i0 < n) prev = pos - len[symbol_at(kind, src, i0 - 1)];
-
 #pragma unroll
-  for (uint32_t k = 0; k < kPerThread; k++) {
-    const uint64_t i = i0 + k;
-    if (i >= n) break;
+  for (uint32_t k = 0; k < kPerThread; k++) mine += i0 + k < n ? len[syms[k]] : 0u;
+  const uint64_t word0 = base >> 5;  // global word of the block's first bit
+  const uint64_t gword0 = ((base >> 6) * kGapBits) >> 5;  // global gap word of its first chunk
+  uint64_t pos = base + block_exclusive(mine, scratch);
+  // positions relative to a tile-aligned origin at or below the block's
+  // first bit fit 32 bits and keep chunk and tile boundaries aligned; the
+  // start of the element before this thread's first one may lie below it
+  const uint64_t org = base & ~(uint64_t)(DF_TILE_BITS - 1);
+  int32_t lpos = (int32_t)(pos - org);
+  int32_t lprev = i0 > 0 && i0 < n ? lpos - (int32_t)len[prev_sym] : lpos;
+  const uint32_t count = full ? kPerThread : i0 < n ? (uint32_t)(n - i0) : 0u;
+
+  // the thread's codes are packed in a register and whole words ORed into
+  // the block buffer (its first and last word are shared with neighbours)
+  const uint64_t lp0 = pos - (word0 << 5);
+  uint32_t wix = (uint32_t)(lp0 >> 5), acc_bits = (uint32_t)(lp0 & 31);
+  uint64_t acc = 0;
+  // kept rolled: unrolled, the kernel needs 76 registers instead of 48 and
+  // ran 8% slower
+  for (uint32_t k = 0; k < count; k++) {
     const uint32_t s = syms[k], l = len[s];
-    if (i == 0) {
+    if (k == 0 && i0 == 0) {
       tile_out[0] = 0;  // gap field 0 is 0: the stream is cleared beforehand
     } else {
-      if ((prev >> 6) != (pos >> 6)) {  // first code of chunk pos / 64
-        const uint64_t t = pos >> 6, g = pos & 63, at = t * kGapBits;
-        const uint32_t sh = (uint32_t)(at & 31);
-        atomicOr(&gaps[at >> 5], (uint32_t)(g << sh));
-        if (sh > 32 - kGapBits) atomicOr(&gaps[(at >> 5) + 1], (uint32_t)(g >> (32 - sh)));
+      if ((lprev >> 6) != (lpos >> 6)) {  // first code of its chunk
+        const uint64_t t = (org >> 6) + (uint64_t)(lpos >> 6), at = t * kGapBits - (gword0 << 5);
+        const uint32_t g = (uint32_t)lpos & 63u, sh = (uint32_t)(at & 31);
+        atomicOr(&gbuf[at >> 5], g << sh);
+        if (sh > 32 - kGapBits) atomicOr(&gbuf[(at >> 5) + 1], g >> (32 - sh));
       }
-      if ((prev >> 14) != (pos >> 14)) tile_out[pos >> 14] = i;  // first code of tile pos / 16384
+      if ((lprev >> 14) != (lpos >> 14))  // first code of its tile
+        tile_out[(org >> 14) + (uint64_t)(lpos >> 14)] = i0 + k;
     }
-    // the code's bits into the block buffer: at most two words
-    const uint64_t lp = pos - (word0 << 5);
-    const uint32_t w = (uint32_t)(lp >> 5), sh = (uint32_t)(lp & 31);
-    const uint64_t v = (uint64_t)rev[s] << sh;
-    atomicOr(&buf[w], (uint32_t)v);
-    if ((uint32_t)(v >> 32)) atomicOr(&buf[w + 1], (uint32_t)(v >> 32));
-    prev = pos;
-    pos += l;
+    // the code's bits after the accumulated ones (acc_bits < 32, l <= 32)
+    acc |= (uint64_t)rev[s] << acc_bits;
+    acc_bits += l;
+    if (acc_bits >= 32) {
+      if ((uint32_t)acc) atomicOr(&buf[wix], (uint32_t)acc);
+      acc >>= 32;
+      acc_bits -= 32;
+      wix++;
+    }
+    lprev = lpos;
+    lpos += (int32_t)l;
   }
+  if (acc_bits && (uint32_t)acc) atomicOr(&buf[wix], (uint32_t)acc);
   if (kind == DF_KIND_BF16) {  // sign|mantissa bytes of this thread's elements
     const uint16_t *u = (const uint16_t *)src;
-    if (i0 + kPerThread <= n) {
+    if (full) {  // from the words already loaded: two elements per word
+      const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
       uint32_t o[kPerThread / 4];
 #pragma unroll
       for (uint32_t q = 0; q < kPerThread / 4; q++) {
         uint32_t x = 0;
 #pragma unroll
         for (uint32_t r = 0; r < 4; r++) {
-          const uint32_t e = u[i0 + 4 * q + r];
+          const uint32_t e = (w[2 * q + (r >> 1)] >> (16 * (r & 1))) & 0xFFFFu;
           x |= (((e >> 8) & 0x80u) | (e & 0x7Fu)) << (8 * r);
         }
         o[q] = x;
@@ -220,6 +325,17 @@ __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src,
       bits[word0 + k] = v;
     }
   }
+  // gap words: a field can straddle two words, so the first two and the last
+  // two may hold fields written by the neighbouring blocks
+  const uint64_t ngw = ((((last_bit - 1) >> 6) * kGapBits + kGapBits - 1) >> 5) - gword0 + 1;
+  for (uint64_t k = threadIdx.x; k < ngw; k += kThreads) {
+    const uint32_t v = gbuf[k];
+    if (k < 2 || k + 2 >= ngw) {
+      if (v) atomicOr(&gaps[gword0 + k], v);
+    } else {
+      gaps[gword0 + k] = v;
+    }
+  }
 }
 
 __global__ void enc_finish(uint64_t *tile_out, uint64_t n_tiles, uint64_t n, uint32_t *max_tile) {
@@ -232,26 +348,32 @@ __global__ void enc_finish(uint64_t *tile_out, uint64_t n_tiles, uint64_t n, uin
 }
 
 uint64_t blocks_for(uint64_t n) { return (n + kBlock - 1) / kBlock; }
+uint64_t segments_for(uint64_t nblocks) { return (nblocks + 1023) / 1024; }
 
 }  // namespace
 
 extern "C" {
 
+uint64_t df_encode_workspace_bytes(uint64_t n) {
+  // block sums, block bases, segment totals
+  return 8 * (2 * (blocks_for(n) + 1) + segments_for(blocks_for(n)) + 1) + 16;
+}
+
 df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint64_t *d_hist,
                               hipStream_t stream) {
-  if (!d_hist || (n && !d_src) || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4))
+  if (!d_hist || (n && (!d_src || ((uintptr_t)d_src & 15))) ||
+      (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4))
     return DF_ERR_ARG;
   hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, stream, (uint32_t *)d_hist, (uint64_t)512);
   if (n) {
-    uint64_t grid = (n + kThreads * 64 - 1) / (kThreads * 64);
-    if (grid > 4096) grid = 4096;
+    uint64_t grid = (n + kThreads * kPerThread * 8 - 1) / (kThreads * kPerThread * 8);
+    if (grid > 2048) grid = 2048;
     hipLaunchKernelGGL(histogram_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, (int)kind, d_src, n,
                        (unsigned long long *)d_hist);
   }
   return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
-uint64_t df_encode_workspace_bytes(uint64_t n) { return 2 * 8 * (blocks_for(n) + 1) + 16; }
 
 df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
                            const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
@@ -260,7 +382,7 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
   if (!lengths || !layout || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4) ||
       layout->kind != kind || layout->n != n || !d_tile_out || !d_max_tile)
     return DF_ERR_ARG;
-  if (n && (!d_src || !d_bitstream || !d_gaps || !d_workspace || ((uintptr_t)d_workspace & 15) ||
+  if (n && (!d_src || ((uintptr_t)d_src & 15) || !d_bitstream || !d_gaps || !d_workspace || ((uintptr_t)d_workspace & 15) ||
             ((uintptr_t)d_bitstream & 15) || ((uintptr_t)d_gaps & 15) || ((uintptr_t)d_tile_out & 7)))
     return DF_ERR_ARG;
   if (kind == DF_KIND_BF16 && n && (!d_sign_mantissa || ((uintptr_t)d_sign_mantissa & 15))) return DF_ERR_ARG;
@@ -307,9 +429,12 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
   }
   const uint64_t nb = blocks_for(n);
   if (nb > 0xFFFFFFFFull) return DF_ERR_ARG;
-  uint64_t *sums = (uint64_t *)d_workspace, *bases = sums + nb + 1;
+  uint64_t *sums = (uint64_t *)d_workspace, *bases = sums + nb + 1, *segs = bases + nb + 1;
+  const uint64_t nseg = segments_for(nb);
   hipLaunchKernelGGL(enc_sums, dim3((uint32_t)nb), dim3(kThreads), 0, stream, (int)kind, d_src, n, cb, sums);
-  hipLaunchKernelGGL(enc_scan, dim3(1), dim3(1024), 0, stream, (const uint64_t *)sums, nb, bases);
+  hipLaunchKernelGGL(enc_scan_local, dim3((uint32_t)nseg), dim3(1024), 0, stream, (const uint64_t *)sums, nb, bases,
+                     segs);
+  hipLaunchKernelGGL(enc_scan_add, dim3((uint32_t)nseg), dim3(1024), 0, stream, bases, nb, (const uint64_t *)segs);
   hipLaunchKernelGGL(enc_write, dim3((uint32_t)nb), dim3(kThreads), 0, stream, (int)kind, d_src, n, cb,
                      (const uint64_t *)bases, (uint32_t *)d_bitstream, (uint32_t *)d_gaps, d_tile_out,
                      d_sign_mantissa);

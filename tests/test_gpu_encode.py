@@ -85,3 +85,13 @@ def test_device_encoder_8b_block(torch_dev):
     layers = synth.u4_block(0)
     _, p, n, _ = layers[4]
     check(torch, dev, 2, p, n)
+
+
+def test_device_encoder_rejects_misaligned_source(torch_dev):
+    # the encoder kernels read 16-byte vectors: a source that does not start
+    # on a 16-byte boundary is refused before any launch
+    torch, dev = torch_dev
+    src = torch.zeros(1000, dtype=torch.int16, device=dev)[1:]
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_histogram_device(dfh.KIND_BF16, src)
+    assert e.value.status == -1
