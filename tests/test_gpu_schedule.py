@@ -107,3 +107,40 @@ def test_graph_replays(torch_dev, block):
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), r
         dfh.df_decompress(dc, eager)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_batched_jobs_each_with_a_slot(torch_dev):
+    # a batched launch splits the grid between its jobs; sixteen containers
+    # of 2.9M-4.4M weights (about 450-700 tiles, each job some 32
+    # workgroups) are each dealt by their own counters, four parts per job
+    # and uneven workgroup counts per part
+    torch, dev = torch_dev
+    rng = np.random.default_rng(5)
+    sizes = [2_900_000 + 100_003 * k for k in range(16)]
+    srcs = [synth.bf16_rne(rng.normal(0, 0.02, n).astype(np.float32)) for n in sizes]
+    cs = [dfh.compress(dfh.KIND_BF16, s) for s in srcs]
+    assert min(c.info()["n_tiles"] for c in cs) > 3 * 32 * 4
+    dcs = [dfh.to_device(c, dev) for c in cs]
+    outs = [dc.empty_output() for dc in dcs]
+    refs = [torch.from_numpy(s.view(np.int16)).to(dev) for s in srcs]
+    for rep in range(3):
+        for o in outs:
+            o.view(torch.int16).fill_(0)
+        dfh.df_decompress_batch(dcs, outs)
+        torch.cuda.synchronize()
+        for k, (o, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(o.view(torch.int16), r), (rep, k)
+
+
+def test_batched_large_jobs(torch_dev, block):
+    # three large jobs in one launch (about 170 workgroups each)
+    torch, dev = torch_dev
+    dc, ref = block
+    outs = [dc.empty_output() for _ in range(3)]
+    for rep in range(3):
+        for o in outs:
+            o.view(torch.int16).fill_(0)
+        dfh.df_decompress_batch([dc, dc, dc], outs)
+        torch.cuda.synchronize()
+        for k, o in enumerate(outs):
+            assert torch.equal(o.view(torch.int16), ref), (rep, k)
