@@ -118,7 +118,7 @@ typedef enum {
 #define DF_MAX_BATCH 16         /* containers per df_decompress_batch launch  */
 
 /* Device error bits written by df_decompress_checked. */
-#define DF_DEVERR_COUNT 1u  /* a tile decodes to a different count than tile_out says */
+#define DF_DEVERR_COUNT 1u  /* a tile (uint8: a pair of tiles) decodes to a different count than tile_out says */
 #define DF_DEVERR_CODE 2u   /* a stream prefix matches no code                      */
 
 typedef struct {
@@ -234,7 +234,9 @@ df_status df_decompress(const df_device_view *v, void *dst, hipStream_t stream);
 /* As df_decompress, and also checks every tile on the device: d_err (one
  * device uint32, zeroed by the caller beforehand) receives the OR of
  * DF_DEVERR_* bits; read it after synchronising the stream.  Output of a
- * tile that fails a check is unspecified; writes stay inside dst. */
+ * tile that fails a check is unspecified; writes stay inside dst.  A uint8
+ * launch decodes tiles in pairs (2p, 2p + 1) and checks each pair against
+ * tile_out[2p] and tile_out[min(2p + 2, n_tiles)]. */
 df_status df_decompress_checked(const df_device_view *v, void *dst, uint32_t *d_err,
                                 hipStream_t stream);
 

@@ -22,13 +22,18 @@
 //   - workgroups are persistent and walk the container in steps of
 //     (groups x workgroups) tiles, in order; the next step's stream words,
 //     gap fields and tile offsets are loaded one step ahead;
+//   - a uint8 group takes two neighbouring tiles per step, each lane two
+//     neighbouring chunks (its threads 2l and 2l + 1, both with their own
+//     gap field): at 6.6-bit codes a chunk holds ten codes, and the step's
+//     fixed cost (loads, offsets, scan, barriers) is then spread over
+//     twenty;
 //   - a group stores a tile one step late: the store pass of tile k shares a
 //     barrier interval with the count of tile k + 1, so HBM traffic overlaps
 //     the decode; the sign|mantissa bytes it merges are requested at the top
 //     of the step, before the count;
-//   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes)
-//     in registers and walks them as a 96-bit window shifted with funnel
-//     shifts;
+//   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes;
+//     uint8: its 16 bytes plus the next 4) in registers and walks each chunk
+//     as a 96-bit window shifted with funnel shifts;
 //   - a lookup in the multi-code table yields up to five codes; codes longer
 //     than 12 bits fall back to the hierarchical tables;
 //   - the per-tile prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus
@@ -74,13 +79,18 @@ constexpr uint32_t kSlack = 12;
 // Table entries phase 1 keeps in registers for phase 2 to replay; a lane
 // with more walks the rest of its chunk again from where the kept ones end.
 // Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
-// 2.7-bit codes), uint8 4 of its pair-table words (every unrolled step costs
-// the whole wave, and the uint8 kernel is bound by VALU issue), BF16 none
+// 2.7-bit codes), uint8 4 of its pair-table words per chunk (every unrolled
+// step costs the whole wave, and the uint8 kernel is bound by VALU issue), BF16 none
 // (its sign|mantissa prefetch holds the registers they would need).
 template <int KIND>
 constexpr uint32_t kKeep = KIND == DF_KIND_U4 ? 7u : KIND == DF_KIND_U8 ? 4u : 0u;
 template <int KIND>
 constexpr uint32_t kKeepRegs = kKeep<KIND> ? kKeep<KIND> : 1u;
+// Stream chunks per lane: a uint8 lane walks two neighbouring chunks (a tile
+// group decodes two tiles per step).  Measured 11% faster on the uint8
+// block; BF16 and uint4 chunks hold 24 codes and keep one.
+template <int KIND>
+constexpr uint32_t kChunks = KIND == DF_KIND_U8 ? 2u : 1u;
 
 struct Job {
   const uint32_t *bits;  // bitstream, little-endian 32-bit words
@@ -376,34 +386,151 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
 }
 
 struct ChunkRegs {
-  uint32_t w0, w1, w2, w3, g0, g1;  // w3: uint4 only (next-tile code, below)
+  // w3: uint4 (next-tile code, below) and uint8 (second chunk); w4: uint8
+  uint32_t w0, w1, w2, w3, w4, g0, g1;
 };
 
-// The stream words and gap fields of one lane of a tile.  Addresses are a
-// wave-uniform base plus a 32-bit lane offset.
-// A tile past the last (a group with no next tile) reads the last tile
+// The stream words and gap fields of one lane of a span (kChunks tiles).
+// Addresses are a wave-uniform base plus a 32-bit lane offset.
+// A span past the last (a group with no next span) reads the last span
 // again: the loads are issued on every path, so each step puts the same
-// number of loads in flight, in the same order.  Needs n_tiles >= 1.
+// number of loads in flight, in the same order.  In a last span of one tile
+// (uint8, odd tile count) the lanes of the missing tile read lane 0's words.
+// Reads stay inside the sections: a lane's lookahead word and its second
+// gap word lie at most four bytes past its tile's end, inside the 16 bytes
+// of padding.  Needs n_tiles >= 1.
 template <int KIND>
-__device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t tile, uint32_t lane) {
-  if (tile >= jb.n_tiles) tile = jb.n_tiles - 1;
+__device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t span, uint32_t lane) {
+  constexpr uint32_t C = kChunks<KIND>;
+  const uint64_t n_spans = (jb.n_tiles + C - 1) / C;
+  if (span >= n_spans) span = n_spans - 1;
+  if (C > 1 && C * span + (C * lane) / kTPB >= jb.n_tiles) lane = 0;
   ChunkRegs c;
-  const uint32_t *bits_t = jb.bits + tile * (2 * kTPB);
-  const uint2 w01 = *(const uint2 *)(bits_t + 2 * lane);
+  const uint32_t *bits_t = jb.bits + span * (2 * C * kTPB);
+  const uint2 w01 = *(const uint2 *)(bits_t + 2 * C * lane);
   c.w0 = w01.x;
   c.w1 = w01.y;
-  if (KIND == DF_KIND_U4) {  // 128 bits (the stream has 16 bytes of padding)
-    const uint2 w23 = *(const uint2 *)(bits_t + 2 * lane + 2);
+  c.w4 = 0;
+  if (KIND == DF_KIND_U4 || C == 2) {  // 128 bits (the stream has 16 bytes of padding)
+    const uint2 w23 = *(const uint2 *)(bits_t + 2 * C * lane + 2);
     c.w2 = w23.x;
     c.w3 = w23.y;
+    if (C == 2) c.w4 = bits_t[4 * lane + 4];
   } else {
     c.w2 = bits_t[2 * lane + 2];
     c.w3 = 0;
   }
-  const uint32_t *gaps_t = jb.gaps + tile * (5 * kTPB / 32);  // 1280 bits per tile
-  c.g0 = gaps_t[(5 * lane) >> 5];
-  c.g1 = gaps_t[((5 * lane) >> 5) + 1];
+  const uint32_t *gaps_t = jb.gaps + span * (5 * C * kTPB / 32);  // 1280 bits per tile
+  c.g0 = gaps_t[(5 * C * lane) >> 5];
+  c.g1 = gaps_t[((5 * C * lane) >> 5) + 1];
   return c;
+}
+
+// Phase 1 over one chunk: counts the codes that start in [gap, E), walking
+// from t (the stream at gap) with rem = E - gap bits before E.  Whole
+// entries are counted; the entry that crosses E gives back its codes that
+// start at or past E (they are the next chunk's first codes).  The walk's
+// first kKeep entries go to registers for phase 2 (symbol words, and the
+// high halves of the high words two to a register) and t is left past them;
+// rem_end is E minus where the walk stopped (<= 0).
+template <int KIND, bool CHECKED>
+__device__ __forceinline__ uint32_t count_chunk(Stream &t, int32_t rem, uint32_t (&kept_lo)[kKeepRegs<KIND>],
+                                                uint32_t (&kept_hi)[(kKeepRegs<KIND> + 1) / 2],
+                                                int32_t &rem_end, uint32_t n_luts, uint32_t *err) {
+  uint32_t cnt = 0, h = 0;
+  // the kept run ends at the lane's first code longer than the table's
+  // index width (kept as an entry of no codes); the loop below resumes the
+  // walk there
+  bool parked = false;
+#pragma unroll
+  for (uint32_t k = 0; k < kKeep<KIND>; k++) {
+    v2u e = {0u, 0u};
+    if (rem > 0 && !parked) {
+      if (KIND == DF_KIND_U8) e.y = lds<const lds_u32>(0)[t.b0 & kPairMask];
+      else e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+      if (e.y < kOneCode) {
+        e = (v2u){0u, 0u};
+        parked = true;
+      } else {
+        drop(t, e.y);
+        rem -= (int32_t)(e.y & 31);
+        cnt += e.y >> 24;
+        h = e.y;
+      }
+    }
+    if (KIND == DF_KIND_U8) {  // a pair-table entry is one word
+      kept_lo[k] = e.y;
+    } else {
+      kept_lo[k] = e.x;
+      if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
+      else kept_hi[k / 2] = e.y >> 16;
+    }
+  }
+  Stream t2 = t;
+  while (rem > 0) {
+    h = KIND == DF_KIND_U8 ? lds<const lds_u32>(0)[t2.b0 & kPairMask]
+                           : lds<const lds_u32>(4)[(t2.b0 & (kDtabEntries - 1)) << 1];
+    if (h < kOneCode) {  // rare: a code longer than the table's index width
+      h = long_entry<KIND, CHECKED>(n_luts, t2, err).y;
+      if ((h & 31) == 0) rem -= 32;
+    }
+    drop(t2, h);
+    rem -= (int32_t)(h & 31);
+    cnt += h >> 24;
+  }
+  if (rem < 0) {
+    // bits of the last entry before E (1..12; a one-code entry has no flags)
+    const uint32_t r = (uint32_t)(rem + (int32_t)(h & 31));
+    if (KIND == DF_KIND_U8) {
+      // a pair: the second code starts at (consumed - its length)
+      if ((h >> 24) == 2 && (h & 31) - lds<const lds_u8>(kPairLens)[(h >> 16) & 0xFFu] >= r) cnt -= 1;
+    } else {
+      cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
+    }
+  }
+  rem_end = rem;
+  return cnt;
+}
+
+// Phase 2 over one chunk: the same entries again (those phase 1 kept are
+// replayed from registers, the rest decoded again from t), their symbol
+// bytes ORed into the staging buffer from byte q until qend.  Returns where
+// the writes stopped (the last entry's codes past qend included).
+template <int KIND, bool CHECKED>
+__device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Stream t,
+                                                const uint32_t (&kept_lo)[kKeepRegs<KIND>],
+                                                const uint32_t (&kept_hi)[(kKeepRegs<KIND> + 1) / 2],
+                                                uint32_t n_luts, uint32_t *err) {
+#pragma unroll
+  for (uint32_t k = 0; k < kKeep<KIND>; k++)
+    if (q < qend) {
+      if (KIND == DF_KIND_U8) {
+        or_pair(q, kept_lo[k]);
+        q += kept_lo[k] >> 24;
+      } else {
+        const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
+        or_entry(q, (v2u){kept_lo[k], hi});
+        q += hi >> 24;
+      }
+    }
+  if (KIND == DF_KIND_U8) {
+    while (q < qend) {
+      uint32_t h = lds<const lds_u32>(0)[t.b0 & kPairMask];
+      if (h < kOneCode) h = long_entry<KIND, CHECKED>(n_luts, t, err).y;  // rare
+      drop(t, h);
+      or_pair(q, h);
+      q += h >> 24;
+    }
+  } else {
+    while (q < qend) {
+      v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
+      if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, err);  // rare
+      drop(t, e.y);
+      or_entry(q, e);
+      q += e.y >> 24;
+    }
+  }
+  return q;
 }
 
 template <int KIND, bool CHECKED>
@@ -446,9 +573,9 @@ void decode_kernel(const Batch batch) {
       dl[i] = i < kTabWords ? dsrc[i] : lsrc[i];
   }
 
-  // Tile schedule.  Static: the job's G = groups x workgroups tile groups
-  // take tiles in order, workgroup w's first tile at step k being
-  // k G + w groups (base).  Dynamic (kDynamic, a counter slot given, more
+  // Tile schedule, in spans of kChunks tiles (one tile but for uint8).
+  // Static: the job's G = groups x workgroups tile groups take spans in
+  // order, workgroup w's first span at step k being k G + w groups (base).  Dynamic (kDynamic, a counter slot given, more
   // than 3G tiles): the first three steps the same; after that the units of
   // `groups` tiles from 3G on are dealt by kParts counters in turn (unit
   // 3 W + P j + c from grab j of counter c, W workgroups, P counters), and a
@@ -460,6 +587,8 @@ void decode_kernel(const Batch batch) {
   // tile, so counter c is grabbed V + W_c times (V grabs with tiles, W_c
   // workgroups); the grab that returns V + W_c - 1 is its last use and
   // stores zero.  Workgroups on faster CUs take more tiles.
+  constexpr uint32_t C = kChunks<KIND>;
+  const uint64_t n_spans = (jb.n_tiles + C - 1) / C;
   const uint64_t step = (uint64_t)jb.wg_count * groups;
   uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
   const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
@@ -473,7 +602,7 @@ void decode_kernel(const Batch batch) {
     const uint32_t oct = nwg >> 3, odd = nwg & 7;  // workgroups of counter c
     const uint32_t wc = 8 * (oct / dyn_parts + (dyn_c < oct % dyn_parts ? 1u : 0u)) +
                         (odd && oct % dyn_parts == dyn_c ? odd : 0u);
-    const uint64_t units = (jb.n_tiles + groups - 1) / groups;
+    const uint64_t units = (n_spans + groups - 1) / groups;
     dyn_first = 3 * nwg + dyn_c;
     const uint64_t vc = units > dyn_first ? (units - dyn_first + dyn_parts - 1) / dyn_parts : 0;
     dyn_last = (uint32_t)(vc + wc - 1);
@@ -483,12 +612,12 @@ void decode_kernel(const Batch batch) {
   bool first_step = true, grabbed = false;
   uint32_t tk = 0;  // the grab in flight (lane 0 of the workgroup)
   ChunkRegs nxt = load_chunk<KIND>(jb, base + grp, lane);
-  // the next tile's first and last output index, one step ahead
+  // the next span's first and last output index, one step ahead
   k_u64 *tout = (k_u64 *)jb.tile_out;
   uint64_t nlo = 0, nhi = 0;
-  if (base + grp < jb.n_tiles) {
-    nlo = tout[base + grp];
-    nhi = tout[base + grp + 1];
+  if (base + grp < n_spans) {
+    nlo = tout[C * (base + grp)];
+    nhi = tout[C * (base + grp) + C < jb.n_tiles ? C * (base + grp) + C : jb.n_tiles];
   }
   {  // the staging buffer starts zero (out_bytes is a multiple of 16)
     lds_v4 *z = lds<lds_v4>(buf);
@@ -505,9 +634,9 @@ void decode_kernel(const Batch batch) {
   uint64_t prev_a = 0;
   uint32_t prev_lo = 0, prev_hi = 0, prev_he = 0, prev_ng = 0, prev_dirty = 0;
 
-  for (; base < jb.n_tiles;) {
-    const uint64_t tile = base + grp;  // wave-uniform
-    const bool active = tile < jb.n_tiles;
+  for (; base < n_spans;) {
+    const uint64_t tile = base + grp;  // the span, wave-uniform
+    const bool active = tile < n_spans;
     // The previous tile's first sign|mantissa granules go in flight first
     // (granules past the tile read its last one; step 0 reads granule 0),
     // then the wait for this step's stream words leaves exactly these loads
@@ -528,13 +657,13 @@ void decode_kernel(const Batch batch) {
     uint64_t lo = nlo, hi = nhi;
     const uint64_t next = (kDynamic<KIND> ? base_nxt : base + step) + grp;  // next step's tile
     nxt = load_chunk<KIND>(jb, next, lane);
-    if (next < jb.n_tiles) {
-      nlo = tout[next];
-      nhi = tout[next + 1];
+    if (next < n_spans) {
+      nlo = tout[C * next];
+      nhi = tout[C * next + C < jb.n_tiles ? C * next + C : jb.n_tiles];
     }
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
-    if (hi - lo > jb.max_tile_elems) hi = lo + jb.max_tile_elems;
+    if (hi - lo > C * jb.max_tile_elems) hi = lo + C * jb.max_tile_elems;
     // output range relative to the store-granule-aligned base a
     const uint64_t a = KIND == DF_KIND_BF16 ? (lo & ~7ull) : KIND == DF_KIND_U8 ? (lo & ~15ull) : (lo & ~31ull);
     const uint32_t lo_r = (uint32_t)(lo - a), hi_r = (uint32_t)(hi - a);
@@ -542,19 +671,25 @@ void decode_kernel(const Batch batch) {
     const uint32_t gsz = KIND == DF_KIND_BF16 ? 8u : KIND == DF_KIND_U8 ? 16u : 32u;
     const uint32_t ngroups = active ? (hi_r + gsz - 1) / gsz : 0u;
 
-    // chunk bounds: codes start in [gap, E) of this lane's 64 stream bits
-    uint32_t gap = 0, E = 0;
+    // chunk bounds: codes start in [gap, E) of this lane's (first) 64
+    // stream bits, and in [gap2, E2) of its second chunk (uint8)
+    uint32_t gap = 0, E = 0, gap2 = 0, E2 = 0;
     if (active) {
-      const uint64_t chunks_left = jb.n_threads - tile * kTPB;  // > 0 for an active tile
-      if (lane < chunks_left) {
-        gap = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * lane) & 31)) & 31u;
-        const uint64_t bits_left = jb.total_bits - tile * (64 * kTPB);
-        if (bits_left >= 64 * (uint64_t)kTPB) {
+      const uint64_t chunks_left = jb.n_threads - tile * (C * kTPB);  // > 0 for an active span
+      if (C * lane < chunks_left) {
+        const uint32_t f = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * C * lane) & 31));
+        gap = f & 31u;
+        const uint64_t bits_left = jb.total_bits - tile * (64 * C * kTPB);
+        if (bits_left >= 64 * (uint64_t)(C * kTPB)) {
           E = 64;
+          E2 = C == 2 ? 64u : 0u;
         } else {
-          const uint32_t r = (uint32_t)bits_left - 64 * lane;
+          const uint32_t r = (uint32_t)bits_left - 64 * C * lane;
           E = r < 64 ? r : 64u;
+          if (C == 2) E2 = r < 64 ? 0u : r - 64 < 64 ? r - 64 : 64u;
         }
+        if (C == 2 && C * lane + 1 < chunks_left) gap2 = (f >> 5) & 31u;
+        else E2 = 0;
       }
     }
 
@@ -563,70 +698,21 @@ void decode_kernel(const Batch batch) {
     // SIMD compete for issue, the chains go first and the stores fill in
     // (measured: about 1% on the BF16 block, 3% on uint8).
     __builtin_amdgcn_s_setprio(3);
-    // phase 1: count the codes that start in [gap, E).  Whole entries are
-    // counted; the entry that crosses E gives back its codes that start at
-    // or past E (they are the next lane's first codes).
-    uint32_t cnt = 0;
-    int32_t rem_end = 0;  // E minus where the walk stopped (<= 0)
-    // the walk's first entries, for phase 2: symbol words, and the high
-    // halves of the high words (fifth symbol, code count) two to a register
+    // phase 1: count the codes that start in the lane's chunks
+    int32_t rem_end = 0;  // E minus where the first chunk's walk stopped (<= 0)
     uint32_t kept_lo[kKeepRegs<KIND>], kept_hi[(kKeepRegs<KIND> + 1) / 2];
-    Stream after = stream_at(cur.w0, cur.w1, cur.w2, gap);  // the walk past them
-    {
-      Stream &t = after;
-      int32_t rem = (int32_t)(E - gap);  // bits left before E
-      uint32_t h = 0;
-      // the kept run ends at the lane's first code longer than the table's
-      // index width (kept as an entry of no codes); the loop below resumes
-      // the walk there
-      bool parked = false;
-#pragma unroll
-      for (uint32_t k = 0; k < kKeep<KIND>; k++) {
-        v2u e = {0u, 0u};
-        if (rem > 0 && !parked) {
-          if (KIND == DF_KIND_U8) e.y = lds<const lds_u32>(0)[t.b0 & kPairMask];
-          else e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
-          if (e.y < kOneCode) {
-            e = (v2u){0u, 0u};
-            parked = true;
-          } else {
-            drop(t, e.y);
-            rem -= (int32_t)(e.y & 31);
-            cnt += e.y >> 24;
-            h = e.y;
-          }
-        }
-        if (KIND == DF_KIND_U8) {  // a pair-table entry is one word
-          kept_lo[k] = e.y;
-        } else {
-          kept_lo[k] = e.x;
-          if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
-          else kept_hi[k / 2] = e.y >> 16;
-        }
-      }
-      Stream t2 = t;
-      while (rem > 0) {
-        h = KIND == DF_KIND_U8 ? lds<const lds_u32>(0)[t2.b0 & kPairMask]
-                               : lds<const lds_u32>(4)[(t2.b0 & (kDtabEntries - 1)) << 1];
-        if (h < kOneCode) {  // rare: a code longer than the table's index width
-          h = long_entry<KIND, CHECKED>(n_luts, t2, batch.err).y;
-          if ((h & 31) == 0) rem -= 32;
-        }
-        drop(t2, h);
-        rem -= (int32_t)(h & 31);
-        cnt += h >> 24;
-      }
-      if (rem < 0) {
-        // bits of the last entry before E (1..12; a one-code entry has no flags)
-        const uint32_t r = (uint32_t)(rem + (int32_t)(h & 31));
-        if (KIND == DF_KIND_U8) {
-          // a pair: the second code starts at (consumed - its length)
-          if ((h >> 24) == 2 && (h & 31) - lds<const lds_u8>(kPairLens)[(h >> 16) & 0xFFu] >= r) cnt -= 1;
-        } else {
-          cnt -= (h >> 24) - 1 - __popc(__builtin_amdgcn_ubfe(h, 5, (r - 1) & 15));
-        }
-      }
-      rem_end = rem;
+    Stream after = stream_at(cur.w0, cur.w1, cur.w2, gap);  // the walk past the kept entries
+    uint32_t cnt = count_chunk<KIND, CHECKED>(after, (int32_t)(E - gap), kept_lo, kept_hi, rem_end, n_luts,
+                                             batch.err);
+    // the second chunk (uint8): words w2..w4, codes from 64 + gap2
+    uint32_t cnt1 = cnt;
+    uint32_t kept2_lo[kKeepRegs<KIND>], kept2_hi[(kKeepRegs<KIND> + 1) / 2];
+    Stream after2 = {0u, 0u, 0u};
+    if constexpr (C == 2) {
+      int32_t rem_end2 = 0;
+      after2 = stream_at(cur.w2, cur.w3, cur.w4, gap2);
+      cnt += count_chunk<KIND, CHECKED>(after2, (int32_t)(E2 - gap2), kept2_lo, kept2_hi, rem_end2, n_luts,
+                                        batch.err);
     }
 
     __builtin_amdgcn_s_setprio(0);
@@ -667,7 +753,7 @@ void decode_kernel(const Batch batch) {
         base_nxt2 = g == 0xFFFFFFFFu ? ~0ull : (uint64_t)groups * (dyn_first + (uint64_t)dyn_parts * g);
       }
       first_step = false;
-      grabbed = dyn && base_nxt2 < jb.n_tiles;
+      grabbed = dyn && base_nxt2 < n_spans;
       if (grabbed && tid == 0) tk = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     const lds_u32 *ws = wsum + 4 * grp;
@@ -700,37 +786,12 @@ void decode_kernel(const Batch batch) {
         qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
       }
-      // the entries phase 1 kept, in walk order, then (rare) the rest of
-      // the walk from where they end
-#pragma unroll
-      for (uint32_t k = 0; k < kKeep<KIND>; k++)
-        if (q < qend) {
-          if (KIND == DF_KIND_U8) {
-            or_pair(q, kept_lo[k]);
-            q += kept_lo[k] >> 24;
-          } else {
-            const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
-            or_entry(q, (v2u){kept_lo[k], hi});
-            q += hi >> 24;
-          }
-        }
-      Stream t = after;
-      if (KIND == DF_KIND_U8) {
-        while (q < qend) {
-          uint32_t h = lds<const lds_u32>(0)[t.b0 & kPairMask];
-          if (h < kOneCode) h = long_entry<KIND, CHECKED>(n_luts, t, batch.err).y;  // rare
-          drop(t, h);
-          or_pair(q, h);
-          q += h >> 24;
-        }
+      if constexpr (C == 2) {  // the first chunk's codes, then the second's
+        const uint32_t q1 = q + cnt1 < qend ? q + cnt1 : qend;
+        write_chunk<KIND, CHECKED>(q, q1, after, kept_lo, kept_hi, n_luts, batch.err);
+        q = write_chunk<KIND, CHECKED>(q1, qend, after2, kept2_lo, kept2_hi, n_luts, batch.err);
       } else {
-        while (q < qend) {
-          v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
-          if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, batch.err);  // rare
-          drop(t, e.y);
-          or_entry(q, e);
-          q += e.y >> 24;
-        }
+        q = write_chunk<KIND, CHECKED>(q, qend, after, kept_lo, kept_hi, n_luts, batch.err);
       }
       // uint4: a tile that ends at an odd element shares its last output
       // byte with the next tile, and writes that whole byte, so it needs the
@@ -883,20 +944,22 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     const uint32_t m = count - base < DF_MAX_BATCH ? count - base : DF_MAX_BATCH;
     Batch b;
     memset(&b, 0, sizeof b);
+    // tiles per lane group and step: kChunks for the kind
+    const uint32_t span_tiles = kind == DF_KIND_U8 ? kChunks<DF_KIND_U8> : 1u;
     uint32_t max_elems = 0, max_luts = 1;
-    uint64_t tiles = 0;
+    uint64_t spans = 0;
     uint32_t nj = 0;
     uint32_t idx[DF_MAX_BATCH];
     for (uint32_t i = 0; i < m; i++) {
       const df_device_view &v = views[base + i];
       if (v.n == 0) continue;
       idx[nj++] = base + i;
-      tiles += v.n_tiles;
+      spans += (v.n_tiles + span_tiles - 1) / span_tiles;
       if (v.max_tile_elems > max_elems) max_elems = v.max_tile_elems;
       if (v.n_luts > max_luts) max_luts = v.n_luts;
     }
     if (nj == 0) continue;
-    const uint32_t out_bytes = out_bytes_for(kind, max_elems);
+    const uint32_t out_bytes = out_bytes_for(kind, span_tiles * max_elems);
     const uint32_t lut_bytes = max_luts * 512;
     // tile groups per workgroup: the choice that keeps the most waves
     // resident per CU (LDS is the limit: the tables are shared per workgroup)
@@ -924,8 +987,9 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     uint32_t wg = 0;
     for (uint32_t k = 0; k < nj; k++) {
       const df_device_view &v = views[idx[k]];
-      uint64_t share = budget * v.n_tiles / tiles;
-      const uint64_t need = (v.n_tiles + groups - 1) / groups;
+      const uint64_t v_spans = (v.n_tiles + span_tiles - 1) / span_tiles;
+      uint64_t share = budget * v_spans / spans;
+      const uint64_t need = (v_spans + groups - 1) / groups;
       if (share < 1) share = 1;
       if (share > need) share = need;
       Job &jb = b.job[k];

@@ -259,6 +259,79 @@ def test_corrupt_tile_is_contained(torch_dev, checked):
     assert np.array_equal(got[hi:], src[hi:])
 
 
+def u8_normal(n, seed, asym=False):
+    return synth.quantize_u8(np.random.default_rng(seed).normal(0, 1, n).astype(np.float32), asym)
+
+
+def test_u8_tile_pairs_odd_and_even_tile_counts(torch_dev, orc):
+    # a uint8 lane group decodes two tiles per step, each lane two
+    # neighbouring chunks: containers of 1..9 tiles (a last pair of one tile
+    # when the count is odd), streams ending inside a lane's first and
+    # second chunk, checked and unchecked
+    counts = set()
+    for i, n in enumerate([2000, 2600, 5100, 7700, 9900, 12_600, 17_700, 19_999, 22_222]):
+        src = u8_normal(n, 300 + i, i % 2 == 1)
+        c = check(torch_dev, orc, 1, src, checked=i % 2 == 0)
+        counts.add(int(c.info()["n_tiles"]) % 2)
+    assert counts == {0, 1}
+
+
+def test_u8_chunk_pairs_split_by_stream_end(torch_dev, orc):
+    # 8-bit codes: the stream ends exactly at a chunk end, so the last lane
+    # has its first chunk only (n_threads odd) or both (n_threads even)
+    for n in (8 * 129, 8 * 130, 2048 + 8, 2048 * 3 - 8, 2048 * 3 + 8):
+        src = np.tile(np.arange(256, dtype=np.uint8), n // 256 + 1)[:n]
+        c = check(torch_dev, orc, 1, src)
+        assert c.info()["total_bits"] == 8 * n
+
+
+def test_u8_checked_reports_bad_tile_offsets(torch_dev):
+    # error path forced from the host, as for BF16: the offset where a tile
+    # pair starts edited on the device (a uint8 launch reads the offsets of
+    # pair starts only, tile_out[2p])
+    torch, dev = torch_dev
+    dc = dfh.to_device(dfh.compress(1, u8_normal(200_000, 6)), dev)
+    to = dc.sections["tile_out"].view(torch.int64)
+    to[2] += 1
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dfh.df_decompress_checked(dc, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & dfh.DEVERR_COUNT
+
+
+@pytest.mark.parametrize("checked", [True, False])
+def test_u8_corrupt_tile_is_contained(torch_dev, checked):
+    # as for BF16, with uint8 tile pairs: every element outside the corrupt
+    # tile's pair and the pair before it is exact.  The lane's bits are set
+    # to ones, which decode as the longest code (24 bits here), so its code
+    # count drops to three; zero bits would decode as the shortest code,
+    # 6 bits, about as many codes as the real stream holds
+    torch, dev = torch_dev
+    src = u8_normal(12_000_000, 13)
+    c = dfh.compress(1, src)
+    nt = int(c.info()["n_tiles"])
+    assert nt > 4096
+    to = np.asarray(c.section("tile_out")).astype(np.int64)
+    dc = dfh.to_device(c, dev)
+    t = nt // 3
+    bits = dc.sections["bitstream"].view(torch.int32)
+    bits[t * 512 + 300: t * 512 + 302] = -1
+    out = dc.empty_output()
+    if checked:
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        dfh.df_decompress_checked(dc, out, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) != 0
+    else:
+        dfh.df_decompress(dc, out)
+    got = host_of(out, 1)
+    p = t // 2 * 2
+    lo, hi = int(to[max(p - 2, 0)]), int(to[min(p + 2, nt)])
+    assert np.array_equal(got[:lo], src[:lo])
+    assert np.array_equal(got[hi:], src[hi:])
+
+
 def test_rejects_bad_arguments(torch_dev):
     torch, dev = torch_dev
     dc = dfh.to_device(dfh.compress(0, bf16_normal(1000, 1)), dev)
