@@ -432,9 +432,10 @@ def forward_overlap(torch, dev, args):
 
 
 def encode_bench(torch, dev, args):
-    """Device encoder (compress_device: device histogram, host codebook and
-    tables, device encode) against the host encoder (compress, all host
-    threads) on the workload's containers; sections must be identical."""
+    """Device encoder (compress_device_batch over the workload's containers:
+    device histograms, host codebooks and tables, device encodes, two reads
+    back to the host in all) against the host encoder (compress, all host
+    threads); sections must be identical."""
     import lossless_entropy_coded_huffman_amd as dfh
     kind, srcs, wconf, _ = make_workload(args.workload, args.seed)
     n = sum(src_elems(kind, s) for s in srcs)
@@ -465,13 +466,13 @@ def encode_bench(torch, dev, args):
     mt = torch.zeros(1, dtype=torch.int32, device=dev)
     dcs = None
     for _ in range(3):   # warm-up
-        dcs = [dfh.compress_device(kind, t, n=k) for t, k in zip(dsrc, nn)]
+        dcs = dfh.compress_device_batch(kind, dsrc, ns=nn if kind == 2 else None)
     torch.cuda.synchronize()
     e2e, kern = [], []
     stream = torch.cuda.current_stream(dev)
     for _ in range(10):
         t0 = time.perf_counter()
-        dcs = [dfh.compress_device(kind, t, n=k) for t, k in zip(dsrc, nn)]
+        dcs = dfh.compress_device_batch(kind, dsrc, ns=nn if kind == 2 else None)
         torch.cuda.synchronize()
         e2e.append(time.perf_counter() - t0)
         # the encode kernels alone, into the same sections

@@ -403,29 +403,98 @@ def compress_device(kind: int, src: torch.Tensor, max_len: int = MAX_LEN, n=None
     """Encode device-resident elements on the GPU: device histogram, codebook
     and tables on the host, device encode.  The sections equal compress()'s.
     For uint4, src is the packed bytes and n the element count."""
-    n = _device_elements(kind, src, n)
-    hist = df_histogram_device(kind, src, n, stream).cpu().numpy().view(np.uint64)
-    lengths = df_build_codebook(hist, max_len)
-    last = 0
-    if n:
-        if kind == KIND_BF16:
-            last = (int(src.view(torch.int16)[n - 1].item()) >> 7) & 0xFF
-        elif kind == KIND_U8:
-            last = int(src[n - 1].item())
-        else:
-            last = (int(src[(n - 1) // 2].item()) >> (4 * ((n - 1) & 1))) & 0xF
-    layout = df_encode_layout(kind, n, hist, last, lengths)
-    inf = _info_dict(layout)
-    sec = {name: torch.empty(max(inf["section_bytes"][name], 16), dtype=torch.uint8, device=src.device)
-           for name in SECTION_NAMES}
-    lut, _, dtab = df_build_tables(kind, lengths)
-    sec["lut"][: lut.nbytes].copy_(torch.from_numpy(lut.view(np.uint8)))
-    sec["dtab"][: dtab.nbytes].copy_(torch.from_numpy(dtab.view(np.uint8)))
-    ws = torch.empty(max(df_encode_workspace_bytes(n), 16), dtype=torch.uint8, device=src.device)
-    max_tile = torch.zeros(1, dtype=torch.int32, device=src.device)
-    df_encode_device(kind, src, n, lengths, layout, sec, ws, max_tile, stream)
-    inf["max_tile_elems"] = int(max_tile.item())
-    return DeviceContainer(None, src.device, _info=inf, _sections=sec)
+    return compress_device_batch(kind, [src], max_len, None if n is None else [n], stream)[0]
+
+
+def compress_device_batch(kind: int, srcs, max_len: int = MAX_LEN, ns=None, stream=None) -> list:
+    """compress_device over several tensors of one kind (the layers of a
+    block) with two reads back to the host in all: the histograms and last
+    symbols in one copy after the histogram launches, the largest tile sizes
+    in one copy after every encode launch.  Codebooks, layouts and tables
+    are built on the host between them; the tables go to the device in one
+    copy from pinned memory.  Every step runs on `stream` (default: the
+    current stream)."""
+    srcs = list(srcs)
+    if not srcs:
+        return []
+    dev = srcs[0].device
+    ns = [_device_elements(kind, t, k) for t, k in zip(srcs, ns if ns is not None else [None] * len(srcs))]
+    ts = _torch_stream(stream, dev)
+    k = len(srcs)
+    with torch.cuda.stream(ts):
+        hists = torch.empty((k, 256), dtype=torch.int64, device=dev)
+        lasts = torch.zeros(k, dtype=torch.int64, device=dev)
+        for i, (t, n) in enumerate(zip(srcs, ns)):
+            _check(lib().df_histogram_device(kind, ctypes.c_void_p(t.data_ptr()), n,
+                                             ctypes.c_void_p(hists[i].data_ptr()), ctypes.c_void_p(ts.cuda_stream)),
+                   "df_histogram_device")
+            if n:   # the element whose symbol ends the stream (uint4: its byte)
+                if kind == KIND_BF16:
+                    lasts[i] = t.view(torch.int16)[n - 1]
+                elif kind == KIND_U8:
+                    lasts[i] = t[n - 1]
+                else:
+                    lasts[i] = t[(n - 1) // 2]
+        back = torch.cat([hists.view(-1), lasts]).cpu().numpy()
+
+        def host_part(i):   # codebook, layout and tables of container i
+            n = ns[i]
+            hist = back[256 * i: 256 * i + 256].view(np.uint64)
+            v = int(back[256 * k + i])
+            last = ((v & 0xFFFF) >> 7) & 0xFF if kind == KIND_BF16 else \
+                (v & 0xFF) if kind == KIND_U8 else ((v & 0xFF) >> (4 * ((n - 1) & 1))) & 0xF
+            lengths = df_build_codebook(hist, max_len)
+            lay = df_encode_layout(kind, n, hist, last if n else 0, lengths)
+            lut, _, dtab = df_build_tables(kind, lengths)
+            return lay, lengths, (lut.view(np.uint8), dtab.view(np.uint8))
+
+        parts = [host_part(i) for i in range(k)]
+        lays = [p[0] for p in parts]
+        infos = [_info_dict(p[0]) for p in parts]
+        lens = [p[1] for p in parts]
+        tabs = [p[2] for p in parts]
+        # every container's LUT and DTAB in one pinned buffer, one copy; each
+        # section is a 256-byte aligned view of the device copy
+        offs, tot = [], 0
+        for lut, dtab in tabs:
+            offs.append((tot, tot + _round256(max(lut.size, 16))))
+            tot = offs[-1][1] + _round256(max(dtab.size, 16))
+        pinned = torch.zeros(tot, dtype=torch.uint8, pin_memory=True)
+        pv = pinned.numpy()
+        for (lut, dtab), (a, b) in zip(tabs, offs):
+            pv[a: a + lut.size] = lut
+            pv[b: b + dtab.size] = dtab
+        tables = pinned.to(dev, non_blocking=True)
+        ws = torch.empty(max(max(df_encode_workspace_bytes(n) for n in ns), 16), dtype=torch.uint8, device=dev)
+        max_tiles = torch.zeros(k, dtype=torch.int32, device=dev)
+        secs = []
+        for i, (t, n) in enumerate(zip(srcs, ns)):
+            inf = infos[i]
+            sec = {name: torch.empty(max(inf["section_bytes"][name], 16), dtype=torch.uint8, device=dev)
+                   for name in SECTION_NAMES if name not in ("lut", "dtab")}
+            (lut, dtab), (a, b) = tabs[i], offs[i]
+            sec["lut"] = tables[a: a + max(lut.size, 16)]
+            sec["dtab"] = tables[b: b + max(dtab.size, 16)]
+            df_encode_device(kind, t, n, lens[i], lays[i], sec, ws, max_tiles[i: i + 1], ts)
+            secs.append({name: sec[name] for name in SECTION_NAMES})
+        mt = max_tiles.cpu().numpy()
+    out = []
+    for i in range(k):
+        infos[i]["max_tile_elems"] = int(mt[i])
+        out.append(DeviceContainer(None, dev, _info=infos[i], _sections=secs[i]))
+    return out
+
+
+def _round256(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+def _torch_stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def _stream_handle(stream, device):

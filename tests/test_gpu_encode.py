@@ -95,3 +95,34 @@ def test_device_encoder_rejects_misaligned_source(torch_dev):
     with pytest.raises(dfh.DFError) as e:
         dfh.df_histogram_device(dfh.KIND_BF16, src)
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_device_encoder_batch_on_a_side_stream(torch_dev, kind):
+    # compress_device_batch: one histogram read-back and one tile-size
+    # read-back for all containers, tables through one pinned copy; run on a
+    # stream other than the current one, with an empty container among them
+    torch, dev = torch_dev
+    sizes = [70_001, 0, 1, 16_385, 1_000_001, 4096]
+    hosts = [host_input(kind, n, 500 + i) for i, n in enumerate(sizes)]
+    ts = [device_tensor(torch, dev, kind, a) for a in hosts]
+    nn = sizes if kind == dfh.KIND_U4 else None
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    dcs = dfh.compress_device_batch(kind, ts, ns=nn, stream=side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    for a, n, dc in zip(hosts, sizes, dcs):
+        host = dfh.compress(kind, a, n=n if kind == dfh.KIND_U4 else None)
+        hi = host.info()
+        for k in ("n", "total_bits", "n_threads", "n_tiles", "n_luts", "max_tile_elems"):
+            assert dc.info[k] == hi[k], k
+        for name in dfh.SECTION_NAMES:
+            size = hi["section_bytes"][name]
+            got = dc.sections[name][:size].cpu().numpy()
+            assert np.array_equal(got, np.asarray(host.section(name)).view(np.uint8)), name
+        if n:
+            out = dc.empty_output()
+            dfh.df_decompress(dc, out)
+            want = a.view(np.int16) if kind == dfh.KIND_BF16 else a
+            got = out.view(torch.int16) if kind == dfh.KIND_BF16 else out
+            assert torch.equal(got, torch.from_numpy(want).to(dev))
