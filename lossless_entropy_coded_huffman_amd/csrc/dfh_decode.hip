@@ -350,7 +350,10 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
       const uint32_t e0 = 8 * g;
       const v2u ex = ex_t[g];
       ex_t[g] = (v2u){0u, 0u};
-      const uint2 sv = load_nt2(sm_t + e0);
+      // a plain load: this loop runs only for tiles of more than 8192
+      // elements, and with a non-temporal load here the compiler kept 64-bit
+      // addresses that spilled a register to scratch
+      const uint2 sv = *(const uint2 *)(sm_t + e0);
       const uint2 o01 = merge4(ex.x, sv.x);
       const uint2 o23 = merge4(ex.y, sv.y);
       const uint4 o = make_uint4(o01.x, o01.y, o23.x, o23.y);
