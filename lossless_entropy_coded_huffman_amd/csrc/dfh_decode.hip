@@ -605,22 +605,26 @@ void decode_kernel(const Batch batch) {
   uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
   const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
   uint64_t base_nxt = base + step;  // the workgroup's first tile next step
-  uint32_t dyn_c = 0, dyn_parts = 1, dyn_last = 0, dyn_first = 0;
-  uint32_t *ctr = nullptr;
-  if (dyn) {
-    const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
-    dyn_parts = nwg / 8 < kParts ? (nwg / 8 ? nwg / 8 : 1u) : kParts;
-    dyn_c = (w >> 3) % dyn_parts;
-    const uint32_t oct = nwg >> 3, odd = nwg & 7;  // workgroups of counter c
-    const uint32_t wc = 8 * (oct / dyn_parts + (dyn_c < oct % dyn_parts ? 1u : 0u)) +
-                        (odd && oct % dyn_parts == dyn_c ? odd : 0u);
-    const uint64_t units = (n_spans + groups - 1) / groups;
-    dyn_first = 3 * nwg + dyn_c;
-    const uint64_t vc = units > dyn_first ? (units - dyn_first + dyn_parts - 1) / dyn_parts : 0;
-    dyn_last = (uint32_t)(vc + wc - 1);
-    ctr = g_tickets + ((size_t)jb.ticket * kParts + dyn_c) * kCounterStride;
-  }
+  // the one lane that grabs (thread 0) keeps the counter's constants in LDS:
+  // words 0..1 the published first tile, 2..3 the counter's address, 4 the
+  // first unit, 5 the unit stride, 6 the counter's last value
   lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 16 * groups);
+  if (dyn && tid == 0) {
+    const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
+    const uint32_t parts = nwg / 8 < kParts ? (nwg / 8 ? nwg / 8 : 1u) : kParts;
+    const uint32_t c = (w >> 3) % parts;
+    const uint32_t oct = nwg >> 3, odd = nwg & 7;  // workgroups of counter c
+    const uint32_t wc = 8 * (oct / parts + (c < oct % parts ? 1u : 0u)) + (odd && oct % parts == c ? odd : 0u);
+    const uint64_t units = (n_spans + groups - 1) / groups;
+    const uint32_t first = 3 * nwg + c;
+    const uint64_t vc = units > first ? (units - first + parts - 1) / parts : 0;
+    const uint64_t cp = (uint64_t)(uintptr_t)(g_tickets + ((size_t)jb.ticket * kParts + c) * kCounterStride);
+    nx_lds[2] = (uint32_t)cp;
+    nx_lds[3] = (uint32_t)(cp >> 32);
+    nx_lds[4] = first;
+    nx_lds[5] = parts;
+    nx_lds[6] = (uint32_t)(vc + wc - 1);
+  }
   bool first_step = true, grabbed = false;
   uint32_t tk = 0;  // the grab in flight (lane 0 of the workgroup)
   ChunkRegs nxt = load_chunk<KIND>(jb, base + grp, lane);
@@ -746,13 +750,15 @@ void decode_kernel(const Batch batch) {
     const uint32_t wid = tid >> 6;
     const uint32_t x = wave_inclusive_sum(cnt);
     if ((tid & 63) == 63) wsum[wid] = x;
-    if (dyn && tid == 0) {  // last step's grab, for the workgroup
-      uint32_t pub = 0xFFFFFFFFu;
+    if (dyn && tid == 0) {  // last step's grab, for the workgroup: its first tile
+      uint64_t pub = ~0ull;
       if (grabbed) {
-        pub = tk;
-        if (tk == dyn_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        uint32_t *ctr = (uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]);
+        if (tk == nx_lds[6]) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        pub = (uint64_t)groups * (nx_lds[4] + (uint64_t)nx_lds[5] * tk);
       }
-      *nx_lds = pub;
+      nx_lds[0] = (uint32_t)pub;
+      nx_lds[1] = (uint32_t)(pub >> 32);
     }
     __syncthreads();
     // the workgroup's first tile two steps ahead, then the grab for three
@@ -760,17 +766,20 @@ void decode_kernel(const Batch batch) {
     uint64_t base_nxt2 = 0;
     if constexpr (kDynamic<KIND>) {
       base_nxt2 = base_nxt + step;
-      if (dyn && !first_step) {
-        const uint32_t g = __builtin_amdgcn_readfirstlane(*nx_lds);
-        base_nxt2 = g == 0xFFFFFFFFu ? ~0ull : (uint64_t)groups * (dyn_first + (uint64_t)dyn_parts * g);
-      }
+      if (dyn && !first_step)
+        base_nxt2 = ((uint64_t)__builtin_amdgcn_readfirstlane(nx_lds[1]) << 32) |
+                    __builtin_amdgcn_readfirstlane(nx_lds[0]);
       first_step = false;
       grabbed = dyn && base_nxt2 < n_spans;
-      if (grabbed && tid == 0) tk = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (grabbed && tid == 0)
+        tk = __hip_atomic_fetch_add((uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]), 1u,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     const lds_u32 *ws = wsum + 4 * grp;
     const uint32_t s0 = ws[0], s1 = ws[1], s2 = ws[2], s3 = ws[3];
-    const uint32_t wq = wid & 3;
+    // the wave's index in its group; read as a uniform value in the BF16
+    // kernel, whose compares on it were lane masks kept across the loop
+    const uint32_t wq = (KIND == DF_KIND_BF16 ? __builtin_amdgcn_readfirstlane(wid) : wid) & 3;
     const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
@@ -980,7 +989,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
       const size_t need = (size_t)(kind == DF_KIND_U8 ? kTabBytes<DF_KIND_U8> : kDtabBytes) + lut_bytes +
-                          (size_t)g * out_bytes + 16 * g + 16;
+                          (size_t)g * out_bytes + 16 * g + 32;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
