@@ -21,7 +21,9 @@
 //     512 B each), which lets two 1024-lane workgroups share a CU;
 //   - workgroups are persistent and walk the container in steps of
 //     (groups x workgroups) tiles, in order; the next step's stream words,
-//     gap fields and tile offsets are loaded one step ahead;
+//     gap fields and tile offsets are loaded one step ahead; BF16 keeps that
+//     order for three steps, then workgroups take units of four tiles from
+//     device-side counters, so faster CUs take more;
 //   - a uint8 group takes two neighbouring tiles per step, each lane two
 //     neighbouring chunks (its threads 2l and 2l + 1, both with their own
 //     gap field): at 6.6-bit codes a chunk holds ten codes, and the step's
@@ -34,15 +36,19 @@
 //   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes;
 //     uint8: its 16 bytes plus the next 4) in registers and walks each chunk
 //     as a 96-bit window shifted with funnel shifts;
-//   - a lookup in the multi-code table yields up to five codes; codes longer
-//     than 12 bits fall back to the hierarchical tables;
+//   - a lookup in the multi-code table yields up to five codes (uint8: the
+//     pair table, up to two codes from 13 bits); longer codes fall back to
+//     the hierarchical tables;
 //   - the per-tile prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus
 //     one LDS step across the group's four waves;
-//   - phase 2 ORs the decoded bytes into the group's LDS staging buffer,
+//   - phase 2 ORs the decoded bytes into the group's LDS staging buffer
+//     (uint8: plain byte stores),
 //     whose byte j holds output element (tile start rounded down to the
 //     store granule) + j; the store pass reads aligned LDS words, clears
 //     them, merges the sign|mantissa bytes (BF16), packs nibbles (uint4) and
-//     issues 16-byte global stores, one in flight per lane (BF16);
+//     issues 16-byte global stores, one in flight per lane (BF16),
+//     non-temporal for BF16 and uint4; BF16 also reads its streams
+//     non-temporally;
 //   - the decode loops run at a raised wave priority, the store pass at the
 //     lowest; the uint4 and uint8 kernels replay phase 1's first table
 //     entries from registers in phase 2.
@@ -248,13 +254,18 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
 // 32-bit code, whose length does not fit the five-bit field, drops one
 // stream word here and reports 0 bits (phase 1 takes the 32 bits off its
 // budget itself).
-// ORs a pair-table entry's symbol bytes (bits 8..23) into the staging
-// buffer at byte q.
-__device__ __forceinline__ void or_pair(uint32_t q, uint32_t h) {
-  const uint64_t v = (uint64_t)__builtin_amdgcn_ubfe(h, 8, 16) << ((q & 3) * 8);
-  lds_u32 *w = lds<lds_u32>(q & ~3u);
-  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Stores a pair-table entry's symbol bytes (bits 8..23) at staging byte q:
+// the first always, the second when the entry holds two codes.  uint8 lanes
+// store plain bytes rather than OR words: every byte a lane stores is either
+// its own or the same value the lane that owns it stores (a walk's last
+// entry reaches into the next chunk's first codes), and an entry of no codes
+// (a kept run parked at a long code) stores a zero that the lane's own walk
+// overwrites later; so the staging buffer needs no clearing between tiles.
+// Measured 3.7% faster on the uint8 block than two LDS ORs per entry.
+__device__ __forceinline__ void put_pair(uint32_t q, uint32_t h) {
+  lds_u8 *p = lds<lds_u8>(q);
+  p[0] = (uint8_t)(h >> 8);
+  if (h >= 2u << 24) p[1] = (uint8_t)(h >> 16);
 }
 
 template <int KIND, bool CHECKED>
@@ -311,10 +322,10 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
 // stream and sign|mantissa loads that the decode waits on, and the kernel
 // ran about 5% slower.
 //
-// The pass also leaves the staging buffer zero for the next tile's ORs:
-// each lane clears the granules it has just read, and the bytes from the
-// last granule up to `dirty` (the next lane-group's lookahead slack) are
-// cleared here too.
+// The pass also leaves the staging buffer zero for the next tile's ORs
+// (BF16 and uint4; uint8 stores plain bytes): each lane clears the granules
+// it has just read, and the bytes from the last granule up to `dirty` (the
+// next lane-group's lookahead slack) are cleared here too.
 //
 // uint4 packs a granule of 32 staging bytes into 16 output bytes and owns
 // the bytes whose low-nibble element is its own, [ceil(lo / 2), ceil(hi / 2))
@@ -325,8 +336,9 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
                                            uint32_t hi_r, uint32_t he, uint32_t ngroups, uint32_t dirty,
                                            const uint2 (&smv)[kPrefetch], uint32_t lane) {
   const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : KIND == DF_KIND_U8 ? 16u : 32u;
-  for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
-    *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
+  if (KIND != DF_KIND_U8)  // (uint8 staging is stored plainly, never ORed)
+    for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
+      *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
   if (KIND == DF_KIND_BF16) {
     uint16_t *dst_t = (uint16_t *)jb.dst + a;
     const uint8_t *sm_t = jb.sm + a;
@@ -390,7 +402,6 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
     for (uint32_t g = lane; g < ngroups; g += kTPB) {
       const uint32_t e0 = 16 * g;
       const v4u v = ex_t[g];
-      ex_t[g] = (v4u){0u, 0u, 0u, 0u};
       if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
       else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
     }
@@ -517,7 +528,7 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
   for (uint32_t k = 0; k < kKeep<KIND>; k++)
     if (q < qend) {
       if (KIND == DF_KIND_U8) {
-        or_pair(q, kept_lo[k]);
+        put_pair(q, kept_lo[k]);
         q += kept_lo[k] >> 24;
       } else {
         const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
@@ -530,7 +541,7 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
       uint32_t h = lds<const lds_u32>(0)[t.b0 & kPairMask];
       if (h < kOneCode) h = long_entry<KIND, CHECKED>(n_luts, t, err).y;  // rare
       drop(t, h);
-      or_pair(q, h);
+      put_pair(q, h);
       q += h >> 24;
     }
   } else {
@@ -549,7 +560,8 @@ template <int KIND, bool CHECKED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
   // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
-  // one staging buffer per tile group, then the per-wave scan sums
+  // one staging buffer per tile group, the per-wave scan sums, then eight
+  // words for the dynamic schedule
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
@@ -794,8 +806,8 @@ void decode_kernel(const Batch batch) {
     // the staging buffer until the lane's cnt codes are written.  The entry that crosses the
     // chunk end is not clipped: its codes past the end are the next lane's
     // first codes (code boundaries are a property of the stream), written to
-    // the same positions with the same values by that lane, so the OR is
-    // idempotent; past the tile's last code they land in the staging slack,
+    // the same positions with the same values by that lane, so the OR (the
+    // uint8 store) is idempotent; past the tile's last code they land in the staging slack,
     // which is never stored.  A lane whose codes would not fit the buffer
     // (only with corrupt offsets or stream) skips the phase, so LDS writes
     // stay inside the buffer.
