@@ -253,6 +253,9 @@ __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src,
   // start of the element before this thread's first one may lie below it
   const uint64_t org = base & ~(uint64_t)(DF_TILE_BITS - 1);
   int32_t lpos = (int32_t)(pos - org);
+  // gap bit of the chunk holding local position p, relative to gbuf:
+  // (p >> 6) * kGapBits + gdelta, with gdelta in (-1312, 32): 32-bit math
+  const int32_t gdelta = (int32_t)((org >> 6) * kGapBits - (gword0 << 5));
   int32_t lprev = i0 > 0 && i0 < n ? lpos - (int32_t)len[prev_sym] : lpos;
   const uint32_t count = full ? kPerThread : i0 < n ? (uint32_t)(n - i0) : 0u;
 
@@ -269,19 +272,19 @@ __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src,
       tile_out[0] = 0;  // gap field 0 is 0: the stream is cleared beforehand
     } else {
       if ((lprev >> 6) != (lpos >> 6)) {  // first code of its chunk
-        const uint64_t t = (org >> 6) + (uint64_t)(lpos >> 6), at = t * kGapBits - (gword0 << 5);
-        const uint32_t g = (uint32_t)lpos & 63u, sh = (uint32_t)(at & 31);
+        const uint32_t at = (uint32_t)((lpos >> 6) * (int32_t)kGapBits + gdelta);
+        const uint32_t g = (uint32_t)lpos & 63u, sh = at & 31;
         atomicOr(&gbuf[at >> 5], g << sh);
         if (sh > 32 - kGapBits) atomicOr(&gbuf[(at >> 5) + 1], g >> (32 - sh));
+        if ((lprev >> 14) != (lpos >> 14))  // first code of its tile (a tile starts a chunk)
+          tile_out[(org >> 14) + (uint64_t)(lpos >> 14)] = i0 + k;
       }
-      if ((lprev >> 14) != (lpos >> 14))  // first code of its tile
-        tile_out[(org >> 14) + (uint64_t)(lpos >> 14)] = i0 + k;
     }
     // the code's bits after the accumulated ones (acc_bits < 32, l <= 32)
     acc |= (uint64_t)rev[s] << acc_bits;
     acc_bits += l;
-    if (acc_bits >= 32) {
-      if ((uint32_t)acc) atomicOr(&buf[wix], (uint32_t)acc);
+    if (acc_bits >= 32) {  // (a zero word ORs nothing: no test for it)
+      atomicOr(&buf[wix], (uint32_t)acc);
       acc >>= 32;
       acc_bits -= 32;
       wix++;
