@@ -672,11 +672,14 @@ void decode_kernel(const Batch batch) {
     // step's words go in flight.
     uint2 smv[kPrefetch];
     if (KIND == DF_KIND_BF16) {
-      const uint64_t last = prev_ng ? prev_a + 8 * (uint64_t)(prev_ng - 1) : 0;
+      // a uniform base and 32-bit lane offsets (granules past the tile
+      // read its last one)
+      const uint8_t *sm_a = jb.sm + prev_a;
+      const uint32_t last = prev_ng ? prev_ng - 1 : 0u;
 #pragma unroll
       for (uint32_t k = 0; k < kPrefetch; k++) {
         const uint32_t g = lane + k * kTPB;
-        smv[k] = load_nt2(jb.sm + (g < prev_ng ? prev_a + 8 * (uint64_t)g : last));
+        smv[k] = load_nt2(sm_a + 8 * (g < prev_ng ? g : last));
       }
     }
     const ChunkRegs cur = nxt;
