@@ -220,7 +220,8 @@ typedef struct {
  * on-chip memory.  One launch covers the whole container (the digest's
  * "Descompressao por bloco de transformer": one batch per block).
  * n == 0 enqueues nothing.  DF_ERR_ARG on bad pointers, kind, alignment,
- * or sizes; DF_ERR_HIP when the launch fails.
+ * or sizes (including containers of 2^31 tiles or more, a 4 TiB stream: the
+ * kernels index tiles in 32 bits); DF_ERR_HIP when the launch fails.
  * Scheduling: a BF16 container of more than three steps of tiles (three
  * times the launch's tile groups) is decoded with tiles handed out by
  * device-side counters that the library keeps in its code object (no

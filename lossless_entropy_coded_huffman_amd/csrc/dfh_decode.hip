@@ -423,13 +423,13 @@ struct ChunkRegs {
 // gap word lie at most four bytes past its tile's end, inside the 16 bytes
 // of padding.  Needs n_tiles >= 1.
 template <int KIND>
-__device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t span, uint32_t lane) {
+__device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint32_t span, uint32_t lane) {
   constexpr uint32_t C = kChunks<KIND>;
-  const uint64_t n_spans = (jb.n_tiles + C - 1) / C;
+  const uint32_t n_spans = ((uint32_t)jb.n_tiles + C - 1) / C;
   if (span >= n_spans) span = n_spans - 1;
-  if (C > 1 && C * span + (C * lane) / kTPB >= jb.n_tiles) lane = 0;
+  if (C > 1 && C * span + (C * lane) / kTPB >= (uint32_t)jb.n_tiles) lane = 0;
   ChunkRegs c;
-  const uint32_t *bits_t = jb.bits + span * (2 * C * kTPB);
+  const uint32_t *bits_t = jb.bits + (uint64_t)span * (2 * C * kTPB);
   const uint2 w01 = load_nt2(bits_t + 2 * C * lane);
   c.w0 = w01.x;
   c.w1 = w01.y;
@@ -443,7 +443,7 @@ __device__ __forceinline__ ChunkRegs load_chunk(const Job &jb, uint64_t span, ui
     c.w2 = bits_t[2 * lane + 2];
     c.w3 = 0;
   }
-  const uint32_t *gaps_t = jb.gaps + span * (5 * C * kTPB / 32);  // 1280 bits per tile
+  const uint32_t *gaps_t = jb.gaps + (uint64_t)span * (5 * C * kTPB / 32);  // 1280 bits per tile
   c.g0 = gaps_t[(5 * C * lane) >> 5];
   c.g1 = gaps_t[((5 * C * lane) >> 5) + 1];
   return c;
@@ -612,11 +612,13 @@ void decode_kernel(const Batch batch) {
   // workgroups); the grab that returns V + W_c - 1 is its last use and
   // stores zero.  Workgroups on faster CUs take more tiles.
   constexpr uint32_t C = kChunks<KIND>;
-  const uint64_t n_spans = (jb.n_tiles + C - 1) / C;
-  const uint64_t step = (uint64_t)jb.wg_count * groups;
-  uint64_t base = (uint64_t)(wg - jb.wg_begin) * groups;
+  // tile and span indices are 32-bit (the host takes fewer than 2^31 tiles)
+  const uint32_t n_tiles = (uint32_t)jb.n_tiles;
+  const uint32_t n_spans = (n_tiles + C - 1) / C;
+  const uint32_t step = jb.wg_count * groups;
+  uint32_t base = (wg - jb.wg_begin) * groups;
   const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
-  uint64_t base_nxt = base + step;  // the workgroup's first tile next step
+  uint32_t base_nxt = base + step;  // the workgroup's first tile next step
   // the one lane that grabs (thread 0) keeps the counter's constants in LDS:
   // words 0..1 the published first tile, 2..3 the counter's address, 4 the
   // first unit, 5 the unit stride, 6 the counter's last value
@@ -627,9 +629,9 @@ void decode_kernel(const Batch batch) {
     const uint32_t c = (w >> 3) % parts;
     const uint32_t oct = nwg >> 3, odd = nwg & 7;  // workgroups of counter c
     const uint32_t wc = 8 * (oct / parts + (c < oct % parts ? 1u : 0u)) + (odd && oct % parts == c ? odd : 0u);
-    const uint64_t units = (n_spans + groups - 1) / groups;
+    const uint32_t units = (n_spans + groups - 1) / groups;
     const uint32_t first = 3 * nwg + c;
-    const uint64_t vc = units > first ? (units - first + parts - 1) / parts : 0;
+    const uint32_t vc = units > first ? (units - first + parts - 1) / parts : 0u;
     const uint64_t cp = (uint64_t)(uintptr_t)(g_tickets + ((size_t)jb.ticket * kParts + c) * kCounterStride);
     nx_lds[2] = (uint32_t)cp;
     nx_lds[3] = (uint32_t)(cp >> 32);
@@ -645,7 +647,7 @@ void decode_kernel(const Batch batch) {
   uint64_t nlo = 0, nhi = 0;
   if (base + grp < n_spans) {
     nlo = tout[C * (base + grp)];
-    nhi = tout[C * (base + grp) + C < jb.n_tiles ? C * (base + grp) + C : jb.n_tiles];
+    nhi = tout[C * (base + grp) + C < n_tiles ? C * (base + grp) + C : n_tiles];
   }
   {  // the staging buffer starts zero (out_bytes is a multiple of 16)
     lds_v4 *z = lds<lds_v4>(buf);
@@ -663,7 +665,7 @@ void decode_kernel(const Batch batch) {
   uint32_t prev_lo = 0, prev_hi = 0, prev_he = 0, prev_ng = 0, prev_dirty = 0;
 
   for (; base < n_spans;) {
-    const uint64_t tile = base + grp;  // the span, wave-uniform
+    const uint32_t tile = base + grp;  // the span, wave-uniform
     const bool active = tile < n_spans;
     // The previous tile's first sign|mantissa granules go in flight first
     // (granules past the tile read its last one; step 0 reads granule 0),
@@ -686,11 +688,11 @@ void decode_kernel(const Batch batch) {
     asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1));
     if (KIND == DF_KIND_U4) asm volatile("" ::"v"(cur.w3));
     uint64_t lo = nlo, hi = nhi;
-    const uint64_t next = (kDynamic<KIND> ? base_nxt : base + step) + grp;  // next step's tile
+    const uint32_t next = (kDynamic<KIND> ? base_nxt : base + step) + grp;  // next step's tile
     nxt = load_chunk<KIND>(jb, next, lane);
     if (next < n_spans) {
       nlo = tout[C * next];
-      nhi = tout[C * next + C < jb.n_tiles ? C * next + C : jb.n_tiles];
+      nhi = tout[C * next + C < n_tiles ? C * next + C : n_tiles];
     }
     if (hi > jb.n) hi = jb.n;
     if (lo > hi) lo = hi;
@@ -706,11 +708,11 @@ void decode_kernel(const Batch batch) {
     // stream bits, and in [gap2, E2) of its second chunk (uint8)
     uint32_t gap = 0, E = 0, gap2 = 0, E2 = 0;
     if (active) {
-      const uint64_t chunks_left = jb.n_threads - tile * (C * kTPB);  // > 0 for an active span
+      const uint64_t chunks_left = jb.n_threads - (uint64_t)tile * (C * kTPB);  // > 0 for an active span
       if (C * lane < chunks_left) {
         const uint32_t f = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * C * lane) & 31));
         gap = f & 31u;
-        const uint64_t bits_left = jb.total_bits - tile * (64 * C * kTPB);
+        const uint64_t bits_left = jb.total_bits - (uint64_t)tile * (64 * C * kTPB);
         if (bits_left >= 64 * (uint64_t)(C * kTPB)) {
           E = 64;
           E2 = C == 2 ? 64u : 0u;
@@ -766,24 +768,24 @@ void decode_kernel(const Batch batch) {
     const uint32_t x = wave_inclusive_sum(cnt);
     if ((tid & 63) == 63) wsum[wid] = x;
     if (dyn && tid == 0) {  // last step's grab, for the workgroup: its first tile
-      uint64_t pub = ~0ull;
+      uint32_t pub = 0xFFFFFFFFu;  // no tile: past any span index
       if (grabbed) {
         uint32_t *ctr = (uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]);
         if (tk == nx_lds[6]) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        pub = (uint64_t)groups * (nx_lds[4] + (uint64_t)nx_lds[5] * tk);
+        // a grab past the last unit gives a tile past the end; clamp so the
+        // product cannot wrap into the span range
+        const uint64_t t = (uint64_t)groups * (nx_lds[4] + (uint64_t)nx_lds[5] * tk);
+        pub = t < 0xFFFFFFFFu ? (uint32_t)t : 0xFFFFFFFFu;
       }
-      nx_lds[0] = (uint32_t)pub;
-      nx_lds[1] = (uint32_t)(pub >> 32);
+      nx_lds[0] = pub;
     }
     __syncthreads();
     // the workgroup's first tile two steps ahead, then the grab for three
     // steps ahead (system scope: past the per-XCD L2 caches)
-    uint64_t base_nxt2 = 0;
+    uint32_t base_nxt2 = 0;
     if constexpr (kDynamic<KIND>) {
       base_nxt2 = base_nxt + step;
-      if (dyn && !first_step)
-        base_nxt2 = ((uint64_t)__builtin_amdgcn_readfirstlane(nx_lds[1]) << 32) |
-                    __builtin_amdgcn_readfirstlane(nx_lds[0]);
+      if (dyn && !first_step) base_nxt2 = __builtin_amdgcn_readfirstlane(nx_lds[0]);
       first_step = false;
       grabbed = dyn && base_nxt2 < n_spans;
       if (grabbed && tid == 0)
@@ -922,7 +924,8 @@ df_status check_view(const df_device_view *v, const void *dst) {
   if (!aligned(v->bitstream, 8) || !aligned(v->gaps, 4) || !aligned(v->tile_out, 8) ||
       !aligned(v->lut, 16) || !aligned(v->dtab, 16))
     return DF_ERR_ARG;
-  if (v->n_tiles == 0 || v->n_threads == 0 || v->n_threads > v->n_tiles * DF_THREADS_PER_TILE ||
+  if (v->n_tiles == 0 || v->n_tiles >= (1ull << 31) || v->n_threads == 0 ||
+      v->n_threads > v->n_tiles * DF_THREADS_PER_TILE ||
       v->n_threads <= (v->n_tiles - 1) * DF_THREADS_PER_TILE)
     return DF_ERR_ARG;
   if (v->total_bits <= (v->n_threads - 1) * 64 || v->total_bits > v->n_threads * 64 + DF_MAX_LEN)

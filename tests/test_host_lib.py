@@ -269,3 +269,28 @@ def test_encode_layout_and_tables_match_the_encoder(kind, n):
         assert nl == inf["n_luts"]
         assert np.array_equal(lut, np.asarray(c.section("lut")))
         assert np.array_equal(dtab, np.asarray(c.section("dtab")))
+
+
+def test_decompress_argument_checks_run_before_any_device_call():
+    # the view checks are host-side: a view of 2^31 tiles (the kernels index
+    # tiles in 32 bits) and inconsistent header scalars are rejected with
+    # DF_ERR_ARG before the device is touched; no GPU needed
+    import ctypes
+    L = dfh.lib()
+    fake = 1 << 20   # aligned, never dereferenced by the checks
+    v = dfh.dfh.df_device_view()
+    v.kind = dfh.KIND_U8
+    v.n_luts = 1
+    v.max_tile_elems = 100
+    for name in ("bitstream", "gaps", "tile_out", "lut", "dtab"):
+        setattr(v, name, fake)
+
+    def call(n_tiles, n_threads, total_bits):
+        v.n, v.n_tiles, v.n_threads, v.total_bits = 1000, n_tiles, n_threads, total_bits
+        return L.df_decompress(ctypes.byref(v), ctypes.c_void_p(fake), ctypes.c_void_p(0))
+
+    t = 1 << 31
+    assert call(t, (t - 1) * 256 + 1, ((t - 1) * 256 + 1) * 64 - 10) == -1
+    t = 3
+    assert call(t, 1, 64) == -1                       # n_threads below (n_tiles - 1) * 256
+    assert call(t, 2 * 256 + 1, 40) == -1             # total_bits below the last thread's start
