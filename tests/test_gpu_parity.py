@@ -477,3 +477,28 @@ def test_u4_batch_and_checked(torch_dev, orc):
     torch.cuda.synchronize()
     for (_, p, n, _), o in zip(layers, outs):
         assert np.array_equal(host_of(o, 2), p)
+
+
+def test_u8_random_sizes_and_distributions(torch_dev, orc):
+    # seeded sweep over container sizes (1 element to 40 tiles) and symbol
+    # distributions: quantised normals, uniform bytes, geometric skews whose
+    # rare symbols take long codes (up to 19 bits here; 32-bit codes are
+    # test_codes_of_every_length_up_to_32's), three symbols; every case
+    # bit-exact against the input and the oracle's decode
+    rng = np.random.default_rng(2024)
+    lengths_seen = set()
+    for case in range(36):
+        n = int(rng.integers(1, 120_000)) if case % 3 else int(rng.integers(1, 3000))
+        d = case % 4
+        if d == 0:
+            src = u8_normal(n, 700 + case, case % 8 == 0)
+        elif d == 1:
+            src = rng.integers(0, 256, n).astype(np.uint8)
+        elif d == 2:
+            src = np.minimum(rng.geometric(0.35 + 0.1 * rng.random(), n) - 1, 255).astype(np.uint8)
+        else:
+            src = rng.choice(rng.choice(256, 3, replace=False), n).astype(np.uint8)
+        say("u8 random case", case, n, d)
+        c = check(torch_dev, orc, 1, src, checked=bool(case & 1))
+        lengths_seen.add(int(c.info()["lengths"].max()))
+    assert max(lengths_seen) >= 16 and min(lengths_seen) <= 2
