@@ -502,3 +502,30 @@ def test_u8_random_sizes_and_distributions(torch_dev, orc):
         c = check(torch_dev, orc, 1, src, checked=bool(case & 1))
         lengths_seen.add(int(c.info()["lengths"].max()))
     assert max(lengths_seen) >= 16 and min(lengths_seen) <= 2
+
+
+def test_bf16_random_sizes_and_distributions(torch_dev, orc):
+    # seeded sweep: normals of random scale, Student-t(3) tails, uniformly
+    # random 16-bit patterns (every exponent), near-constant values; small
+    # containers (static tile order) and three of 40-70M weights, which take
+    # the dynamic tile order; every case bit-exact against the input and,
+    # below 8M weights, against the oracle's decode
+    rng = np.random.default_rng(77)
+    big = {5: 40_000_000, 11: 55_000_000, 17: 70_000_000}
+    for case in range(20):
+        n = big.get(case, int(rng.integers(1, 2_000_000)))
+        d = case % 4
+        if d == 0:
+            src = bf16_normal(n, 900 + case, float(rng.uniform(0.002, 0.2)))
+        elif d == 1:
+            src = synth.bf16_rne((rng.standard_t(3, n) * 0.02).astype(np.float32))
+        elif d == 2:
+            src = rng.integers(0, 65536, n).astype(np.uint16)
+        else:
+            src = (0x3F80 + rng.integers(0, 3, n)).astype(np.uint16)
+        say("bf16 random case", case, n, d)
+        if n < 8_000_000:
+            check(torch_dev, orc, 0, src, checked=bool(case & 1))
+        else:
+            got, err = gpu_decode(torch_dev, dfh.compress(0, src), checked=bool(case & 1))
+            assert err == 0 and np.array_equal(got, src)
