@@ -86,8 +86,9 @@ constexpr uint32_t kSlack = 12;
 // with more walks the rest of its chunk again from where the kept ones end.
 // Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
 // 2.7-bit codes), uint8 4 of its pair-table words per chunk (every unrolled
-// step costs the whole wave, and the uint8 kernel is bound by VALU issue), BF16 none
-// (its sign|mantissa prefetch holds the registers they would need).
+// step costs the whole wave, and the uint8 kernel is bound by VALU issue),
+// BF16 none (its sign|mantissa prefetch holds the registers: with one or two
+// kept entries the kernel spills to scratch).
 template <int KIND>
 constexpr uint32_t kKeep = KIND == DF_KIND_U4 ? 7u : KIND == DF_KIND_U8 ? 4u : 0u;
 template <int KIND>
