@@ -600,8 +600,9 @@ void decode_kernel(const Batch batch) {
 
   // Tile schedule, in spans of kChunks tiles (one tile but for uint8).
   // Static: the job's G = groups x workgroups tile groups take spans in
-  // order, workgroup w's first span at step k being k G + w groups (base).  Dynamic (kDynamic, a counter slot given, more
-  // than 3G tiles): the first three steps the same; after that the units of
+  // order, workgroup w's first span at step k being k G + w groups (base).
+  // Dynamic (kDynamic, a counter slot given, more than 3G tiles): the
+  // first three steps the same; after that the units of
   // `groups` tiles from 3G on are dealt by kParts counters in turn (unit
   // 3 W + P j + c from grab j of counter c, W workgroups, P counters), and a
   // workgroup grabs its next unit from counter c = (w / 8) mod P, so every
@@ -621,8 +622,8 @@ void decode_kernel(const Batch batch) {
   const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
   uint32_t base_nxt = base + step;  // the workgroup's first tile next step
   // the one lane that grabs (thread 0) keeps the counter's constants in LDS:
-  // words 0..1 the published first tile, 2..3 the counter's address, 4 the
-  // first unit, 5 the unit stride, 6 the counter's last value
+  // word 0 the published first tile (0xFFFFFFFF: none), 2..3 the counter's
+  // address, 4 the first unit, 5 the unit stride, 6 the counter's last value
   lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 16 * groups);
   if (dyn && tid == 0) {
     const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
@@ -675,8 +676,7 @@ void decode_kernel(const Batch batch) {
     // step's words go in flight.
     uint2 smv[kPrefetch];
     if (KIND == DF_KIND_BF16) {
-      // a uniform base and 32-bit lane offsets (granules past the tile
-      // read its last one)
+      // a uniform base and 32-bit lane offsets
       const uint8_t *sm_a = jb.sm + prev_a;
       const uint32_t last = prev_ng ? prev_ng - 1 : 0u;
 #pragma unroll
@@ -809,14 +809,14 @@ void decode_kernel(const Batch batch) {
     __builtin_amdgcn_s_setprio(3);
     // phase 2: walk the same entries again (those phase 1 kept are replayed
     // from registers, the rest decoded again) and OR their symbol bytes into
-    // the staging buffer until the lane's cnt codes are written.  The entry that crosses the
-    // chunk end is not clipped: its codes past the end are the next lane's
-    // first codes (code boundaries are a property of the stream), written to
-    // the same positions with the same values by that lane, so the OR (the
-    // uint8 store) is idempotent; past the tile's last code they land in the staging slack,
-    // which is never stored.  A lane whose codes would not fit the buffer
-    // (only with corrupt offsets or stream) skips the phase, so LDS writes
-    // stay inside the buffer.
+    // the staging buffer until the lane's cnt codes are written.  The entry
+    // that crosses the chunk end is not clipped: its codes past the end are
+    // the next lane's first codes (code boundaries are a property of the
+    // stream), written to the same positions with the same values by that
+    // lane, so the OR (the uint8 store) is idempotent; past the tile's last
+    // code they land in the staging slack, which is never stored.  A lane
+    // whose codes would not fit the buffer (only with corrupt offsets or
+    // stream) skips the phase, so LDS writes stay inside the buffer.
     {
       uint32_t q = buf + lo_r + off;
       uint32_t qend = q + cnt;

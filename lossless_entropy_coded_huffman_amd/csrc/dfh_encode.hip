@@ -385,8 +385,9 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
   if (!lengths || !layout || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4) ||
       layout->kind != kind || layout->n != n || !d_tile_out || !d_max_tile)
     return DF_ERR_ARG;
-  if (n && (!d_src || ((uintptr_t)d_src & 15) || !d_bitstream || !d_gaps || !d_workspace || ((uintptr_t)d_workspace & 15) ||
-            ((uintptr_t)d_bitstream & 15) || ((uintptr_t)d_gaps & 15) || ((uintptr_t)d_tile_out & 7)))
+  if (n && (!d_src || ((uintptr_t)d_src & 15) || !d_bitstream || !d_gaps || !d_workspace ||
+            ((uintptr_t)d_workspace & 15) || ((uintptr_t)d_bitstream & 15) || ((uintptr_t)d_gaps & 15) ||
+            ((uintptr_t)d_tile_out & 7)))
     return DF_ERR_ARG;
   if (kind == DF_KIND_BF16 && n && (!d_sign_mantissa || ((uintptr_t)d_sign_mantissa & 15))) return DF_ERR_ARG;
   if (memcmp(layout->lengths, lengths, 256) != 0) return DF_ERR_ARG;
