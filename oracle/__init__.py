@@ -36,8 +36,6 @@ KIND_BF16 = 0
 KIND_U8 = 1
 KIND_U4 = 2
 MAX_LEN = 32
-DTAB_BITS = 12      # multi-code table (BF16, uint4)
-DTAB_BITS_U8 = 13   # pair table (uint8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -88,8 +86,6 @@ def _load():
             "oracle_build_lut": (I, [P, P, I, ctypes.POINTER(I)]),
             "oracle_decode_serial": (I, [I, P, P, U64, U64, P, P]),
             "oracle_decode_tiles": (I, [I, P, P, U64, P, P, U64, U64, P, P, I]),
-            "oracle_check_dtab": (ctypes.c_int64, [I, P, P, I]),
-            "oracle_check_dtab_u8": (ctypes.c_int64, [P, P, I]),
             "oracle_decode_tile_range": (I, [I, P, P, U64, P, P, U64, U64, U64, P, P]),
             "oracle_pack_u4": (I, [P, U64, P]),
         }
@@ -289,22 +285,3 @@ def decode_tile_range(c: dict, b0: int, b1: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("undecodable stream")
     return out
-
-
-def check_dtab(kind: int, lengths, dtab, K: int | None = None) -> int:
-    """Number of entries of a decoder-side table that differ from the
-    definition written in oracle.c: the multi-code table for BF16 and uint4
-    (oracle_check_dtab, K = 12 by default), the pair table and the length
-    bytes after it for uint8 (oracle_check_dtab_u8, K = 13 by default)."""
-    ln = np.ascontiguousarray(lengths, np.uint8)
-    if kind == KIND_U8:
-        K = DTAB_BITS_U8 if K is None else K
-        d = np.ascontiguousarray(dtab).view(np.uint8)
-        if d.size < (4 << K) + 256:
-            raise ValueError("table too short")
-        return int(_load().oracle_check_dtab_u8(_ptr(ln), _ptr(d), int(K)))
-    K = DTAB_BITS if K is None else K
-    d = np.ascontiguousarray(dtab, np.uint64)
-    if d.size < (1 << K):
-        raise ValueError("table too short")
-    return int(_load().oracle_check_dtab(kind, _ptr(ln), _ptr(d), int(K)))

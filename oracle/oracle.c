@@ -723,111 +723,3 @@ int oracle_decode_tile_range(int kind, const uint8_t *lengths, const uint8_t *st
   range_worker(&j);
   return j.status;
 }
-
-/* ------------------------------------------------------------------------ */
-/* Checker for the multi-code decode table that the product library derives
- * from the lengths (a decoder-side accelerator; the pages' own tables are the
- * hierarchical ones above).  Entry w (0 <= w < 2^K) describes the stream
- * whose next K bits are w (first bit = bit 0 of w): the codes that lie
- * entirely inside those K bits, at most five, are decoded in order.  u64
- * entry layout (fields placed so the decoder reads each with one operation):
- *   bits  0..31  symbol bytes of codes 0..3, code i in byte i, unused bytes
- *                zero; for the BF16 kind the byte is the exponent rotated
- *                right by one bit ((e >> 1) | (e & 1) << 7), for uint4 the
- *                symbol itself (the uint8 kind uses the pair table below);
- *   bits 32..36  bits consumed by the codes (sum of their lengths);
- *   bits 37..47  start flags: bit 37 + (j - 1) set when one of the codes
- *                starts at window bit j, for j = 1..11 (the first code
- *                always starts at bit 0);
- *   bits 48..55  symbol byte of code 4 (zero when there are fewer codes);
- *   bits 56..63  number of codes.
- * The entry is zero when the first code is longer than K bits or no code
- * has this prefix.
- * Returns the number of entries that differ from this definition.           */
-/* ------------------------------------------------------------------------ */
-int64_t oracle_check_dtab(int kind, const uint8_t *lengths, const uint64_t *dtab,
-                          int K) {
-  canon_t c;
-  if (K < 1 || K > 12) return -1;
-  if (canon_init(lengths, &c) != 0) return -1;
-  int64_t bad = 0;
-  for (uint64_t w = 0; w < ((uint64_t)1 << K); w++) {
-    uint8_t bits[16];
-    for (int k = 0; k < K; k++) bits[k] = (uint8_t)((w >> k) & 1);
-    uint64_t syms = 0, mask = 0, used = 0, ncodes = 0;
-    uint64_t pos = 0;
-    while (ncodes < 5) {
-      /* bit-serial decode inside the K-bit window */
-      uint64_t code = 0, p = pos;
-      int sym = -1, len = 0;
-      for (int l = 1; l <= O_MAX_LEN && p < (uint64_t)K; l++) {
-        code = (code << 1) | bits[p++];
-        if (c.count[l] && code >= c.first[l] && code - c.first[l] < c.count[l]) {
-          sym = c.sorted[c.offset[l] + (code - c.first[l])];
-          len = l;
-          break;
-        }
-      }
-      if (sym < 0) break;
-      uint8_t b = (uint8_t)sym;
-      if (kind == O_KIND_BF16) b = (uint8_t)((b >> 1) | ((b & 1) << 7));
-      syms |= (uint64_t)b << (8 * ncodes);
-      mask |= (uint64_t)1 << pos;
-      pos += (uint64_t)len;
-      used += (uint64_t)len;
-      ncodes++;
-    }
-    uint64_t expect = (syms & 0xFFFFFFFFull) | (used << 32) | ((mask >> 1) << 37) |
-                      ((syms >> 32) << 48) | (ncodes << 56);
-    if (ncodes == 0) expect = 0;
-    if (dtab[w] != expect) bad++;
-  }
-  return bad;
-}
-
-/*
- * The uint8 pair table (a decoder-side table derived from the code lengths;
- * the container keeps it in its DTAB section for the uint8 kind).  Entry w
- * of 2^K little-endian uint32 words, for the K-bit window w whose bit k is
- * the k-th stream bit: decode whole codes inside the window, at most two;
- *   bits 0..3 bits consumed, 8..15 symbol of code 0, 16..23 symbol of
- *   code 1 (0 when there is one code), 24..31 number of codes;
- *   0 when no code ends inside the window.
- * After the 2^K words follow 256 bytes: the code length of each symbol (0
- * for symbols without a code).  Returns the number of wrong entries plus
- * wrong length bytes; -1 for bad arguments.
- */
-int64_t oracle_check_dtab_u8(const uint8_t *lengths, const uint8_t *section, int K) {
-  canon_t c;
-  if (K < 1 || K > 15) return -1;
-  if (canon_init(lengths, &c) != 0) return -1;
-  int64_t bad = 0;
-  for (uint64_t w = 0; w < ((uint64_t)1 << K); w++) {
-    uint32_t syms[2] = {0, 0}, used = 0, ncodes = 0;
-    uint64_t pos = 0;
-    while (ncodes < 2) {
-      uint64_t code = 0, p = pos;
-      int sym = -1, len = 0;
-      for (int l = 1; l <= O_MAX_LEN && p < (uint64_t)K; l++) {
-        code = (code << 1) | ((w >> p++) & 1);
-        if (c.count[l] && code >= c.first[l] && code - c.first[l] < c.count[l]) {
-          sym = c.sorted[c.offset[l] + (code - c.first[l])];
-          len = l;
-          break;
-        }
-      }
-      if (sym < 0) break;
-      syms[ncodes++] = (uint32_t)sym;
-      pos += (uint64_t)len;
-      used += (uint32_t)len;
-    }
-    uint32_t expect = ncodes ? used | (syms[0] << 8) | (syms[1] << 16) | (ncodes << 24) : 0;
-    const uint8_t *e = section + 4 * w;
-    uint32_t got = (uint32_t)e[0] | ((uint32_t)e[1] << 8) | ((uint32_t)e[2] << 16) | ((uint32_t)e[3] << 24);
-    if (got != expect) bad++;
-  }
-  const uint8_t *tail = section + ((size_t)4 << K);
-  for (int s = 0; s < 256; s++)
-    if (tail[s] != lengths[s]) bad++;
-  return bad;
-}

@@ -426,88 +426,6 @@ def test_corruption_changes_output(orc):
         pass
 
 
-# --------------------------------------------------- multi-code table checker
-def python_dtab(kind, lengths, codes, K):
-    """The multi-code table built by prefix matching over code strings."""
-    strs = code_strings(lengths, codes)
-    inv = {v: k for k, v in strs.items()}
-    tab = np.zeros(1 << K, np.uint64)
-    for w in range(1 << K):
-        bits = "".join(str((w >> k) & 1) for k in range(K))
-        syms, starts, pos, cur = [], [], 0, ""
-        for i, b in enumerate(bits):
-            cur += b
-            if cur in inv:
-                syms.append(inv[cur])
-                starts.append(pos)
-                pos = i + 1
-                cur = ""
-                if len(syms) == 5:
-                    break
-        if not syms:
-            continue
-        v = 0
-        for i, s in enumerate(syms):
-            byte = ((s >> 1) | ((s & 1) << 7)) if kind == 0 else s
-            v |= byte << (8 * i if i < 4 else 48)
-        flags = sum(1 << (st - 1) for st in starts if st > 0)
-        v |= pos << 32 | flags << 37 | len(syms) << 56
-        tab[w] = v
-    return tab
-
-
-def python_dtab_u8(lengths, codes, K):
-    """The uint8 pair table built by prefix matching over code strings, then
-    the 256 code-length bytes."""
-    strs = code_strings(lengths, codes)
-    inv = {v: k for k, v in strs.items()}
-    tab = np.zeros(1 << K, np.uint32)
-    for w in range(1 << K):
-        bits = "".join(str((w >> k) & 1) for k in range(K))
-        syms, pos, cur = [], 0, ""
-        for i, b in enumerate(bits):
-            cur += b
-            if cur in inv:
-                syms.append(inv[cur])
-                pos = i + 1
-                cur = ""
-                if len(syms) == 2:
-                    break
-        if syms:
-            tab[w] = pos | syms[0] << 8 | (syms[1] if len(syms) > 1 else 0) << 16 | len(syms) << 24
-    return np.concatenate([tab.view(np.uint8), np.asarray(lengths, np.uint8)])
-
-
-def test_dtab_u8_checker(orc):
-    # codes of 1..10 bits: windows of 8 bits hold none, one or two whole codes
-    h = np.zeros(256, np.uint64)
-    h[[7, 200, 31, 64, 5, 250, 90, 128, 3, 77, 78]] = [1000, 500, 250, 120, 60, 30, 15, 7, 3, 1, 1]
-    ln = orc.code_lengths(h)
-    K = 8
-    sec = python_dtab_u8(ln, orc.canonical_codes(ln), K)
-    tab = sec[: 4 << K].view(np.uint32)
-    assert (tab >> 24).max() == 2 and ((tab >> 24) == 1).any() and (tab == 0).any()
-    assert orc.check_dtab(1, ln, sec, K) == 0
-    bad = sec.copy()
-    bad[4 * 17 + 1] ^= 1       # a symbol byte
-    bad[(4 << K) + 7] ^= 1     # a length byte
-    assert orc.check_dtab(1, ln, bad, K) == 2
-
-
-@pytest.mark.parametrize("kind", [0, 2])
-def test_dtab_checker(orc, kind):
-    h = np.zeros(256, np.uint64)
-    h[[120, 121, 119, 122, 118, 3, 250]] = [900, 800, 300, 200, 60, 2, 1]
-    ln = orc.code_lengths(h)
-    K = 8
-    tab = python_dtab(kind, ln, orc.canonical_codes(ln), K)
-    assert orc.check_dtab(kind, ln, tab, K) == 0
-    bad = tab.copy()
-    bad[5] ^= np.uint64(1 << 56)
-    bad[200] ^= np.uint64(1)
-    assert orc.check_dtab(kind, ln, bad, K) == 2
-
-
 def test_tile_range_decode_matches_whole(orc):
     rng = np.random.default_rng(21)
     src = bf16_from_f32(rng.normal(0, 0.02, 200_000))
