@@ -557,6 +557,40 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
   return q;
 }
 
+// A decode-table word (16 bytes) on its way to LDS: an entry that claims
+// codes but consumes no bits would never move a walk forward, so it is
+// cleared (a cleared entry sends the walk to the hierarchical tables, which
+// consume at least one bit per code) and, in checked launches, reported as
+// DF_DEVERR_CODE.  Tables built by the library never hold such entries; a
+// caller-made view with a damaged table pointer may.  Entries: BF16 and
+// uint4 two u64 (high words y and w), uint8 four u32 pair entries (the
+// lengths that follow the pair table are left alone).
+template <int KIND, bool CHECKED>
+__device__ __forceinline__ v4u clean_tab(v4u v, uint32_t word, uint32_t *err) {
+  bool bad = false;
+  if (KIND == DF_KIND_U8) {
+    if (word < (4u << DF_DTAB_BITS_U8) / 16) {
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        if (v[c] >= kOneCode && (v[c] & 31u) == 0) {
+          v[c] = 0;
+          bad = true;
+        }
+    }
+  } else {
+    if (v.y >= kOneCode && (v.y & 31u) == 0) {
+      v.x = v.y = 0;
+      bad = true;
+    }
+    if (v.w >= kOneCode && (v.w & 31u) == 0) {
+      v.z = v.w = 0;
+      bad = true;
+    }
+  }
+  if (CHECKED && bad) atomicOr(err, DF_DEVERR_CODE);
+  return v;
+}
+
 template <int KIND, bool CHECKED>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
@@ -590,12 +624,12 @@ void decode_kernel(const Batch batch) {
     const v4u t1 = i1 < total ? (i1 < kTabWords ? dsrc[i1] : lsrc[i1]) : z;
     const v4u t2 = i2 < total ? (i2 < kTabWords ? dsrc[i2] : lsrc[i2]) : z;
     const v4u t3 = i3 < total ? (i3 < kTabWords ? dsrc[i3] : lsrc[i3]) : z;
-    if (i0 < total) dl[i0] = t0;
-    if (i1 < total) dl[i1] = t1;
-    if (i2 < total) dl[i2] = t2;
-    if (i3 < total) dl[i3] = t3;
+    if (i0 < total) dl[i0] = i0 < kTabWords ? clean_tab<KIND, CHECKED>(t0, i0, batch.err) : t0;
+    if (i1 < total) dl[i1] = i1 < kTabWords ? clean_tab<KIND, CHECKED>(t1, i1, batch.err) : t1;
+    if (i2 < total) dl[i2] = i2 < kTabWords ? clean_tab<KIND, CHECKED>(t2, i2, batch.err) : t2;
+    if (i3 < total) dl[i3] = i3 < kTabWords ? clean_tab<KIND, CHECKED>(t3, i3, batch.err) : t3;
     for (uint32_t i = tid + 4 * blockDim.x; i < total; i += blockDim.x)
-      dl[i] = i < kTabWords ? dsrc[i] : lsrc[i];
+      dl[i] = i < kTabWords ? clean_tab<KIND, CHECKED>(dsrc[i], i, batch.err) : lsrc[i];
   }
 
   // Tile schedule, in spans of kChunks tiles (one tile but for uint8).
@@ -820,7 +854,9 @@ void decode_kernel(const Batch batch) {
     {
       uint32_t q = buf + lo_r + off;
       uint32_t qend = q + cnt;
-      const bool fits = lo_r + off + cnt + kSlack <= out_bytes;
+      // (each term is bounded first, so the sum cannot wrap even when a
+      // damaged table makes the counts meaningless)
+      const bool fits = off <= out_bytes && cnt <= out_bytes && lo_r + off + cnt + kSlack <= out_bytes;
       if (!fits) {
         qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
