@@ -491,16 +491,6 @@ def encode_bench(torch, dev, args):
     t0 = time.perf_counter()
     host = [src_compress(dfh, kind, s) for s in srcs]
     t_host = time.perf_counter() - t0
-    def last_symbol(s):
-        if kind == 0:
-            return (int(s.view(np.uint16)[-1]) >> 7) & 0xFF
-        if kind == 1:
-            return int(s[-1])
-        return (int(s[0][(s[1] - 1) // 2]) >> (4 * ((s[1] - 1) & 1))) & 0xF
-
-    lays = [dfh.df_encode_layout(kind, src_elems(kind, s),
-                                 dfh.df_histogram(kind, s[0] if kind == 2 else s, s[1] if kind == 2 else None),
-                                 last_symbol(s), h.info()["lengths"]) for s, h in zip(srcs, host)]
     ws = [torch.empty(max(dfh.df_encode_workspace_bytes(src_elems(kind, s)), 16), dtype=torch.uint8, device=dev)
           for s in srcs]
     mt = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -518,8 +508,8 @@ def encode_bench(torch, dev, args):
         # the encode kernels alone, into the same sections
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for dc, t, k, w, lay, h in zip(dcs, dsrc, nn, ws, lays, host):
-            dfh.df_encode_device(kind, t, dc.n, h.info()["lengths"], lay, dc.sections, w, mt, stream)
+        for dc, t, w in zip(dcs, dsrc, ws):
+            dfh.df_encode_device(kind, t, dc.n, dc.lengths, dc.layout, dc.sections, w, mt, stream)
         b.record(stream)
         torch.cuda.synchronize()
         kern.append(a.elapsed_time(b) * 1e-3)

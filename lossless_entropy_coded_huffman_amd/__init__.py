@@ -9,7 +9,8 @@ with the same names.  ``synth`` draws the seeded synthetic workloads.
 from .dfh import (  # noqa: F401
     KIND_BF16, KIND_U4, KIND_U8, MAX_LEN, SECTION_NAMES, DEVERR_CODE, DEVERR_COUNT, DFError, Container,
     DeviceContainer, compress, compress_device, compress_device_batch, df_build_codebook, df_build_tables, df_encode_device,
-    df_encode_layout, df_encode_workspace_bytes, df_histogram_device, df_container_free, df_container_info,
+    df_encode_layout, df_encode_workspace_bytes, df_histogram_device, df_symbol_device, df_container_free,
+    df_container_info,
     df_container_load, df_container_save, df_container_section, df_container_validate,
     df_decompress, df_decompress_batch, df_decompress_checked, df_encode, df_histogram,
     df_status_string, lib, output_bytes, to_device,

@@ -341,6 +341,11 @@ __global__ __launch_bounds__(kThreads) void enc_write(int kind, const void *src,
   }
 }
 
+// The coded symbol of element i, for the host's layout call.
+__global__ void symbol_kernel(int kind, const void *src, uint64_t i, uint64_t *out) {
+  if (threadIdx.x == 0) *out = symbol_at(kind, src, i);
+}
+
 __global__ void enc_finish(uint64_t *tile_out, uint64_t n_tiles, uint64_t n, uint32_t *max_tile) {
   for (uint64_t b = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; b < n_tiles;
        b += (uint64_t)gridDim.x * blockDim.x) {
@@ -377,6 +382,13 @@ df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint6
   return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
+df_status df_symbol_device(df_kind kind, const void *d_src, uint64_t i, uint64_t *d_sym, hipStream_t stream) {
+  if (!d_src || !d_sym || ((uintptr_t)d_sym & 7) ||
+      (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4))
+    return DF_ERR_ARG;
+  hipLaunchKernelGGL(symbol_kernel, dim3(1), dim3(64), 0, stream, (int)kind, d_src, i, d_sym);
+  return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
 
 df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
                            const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,

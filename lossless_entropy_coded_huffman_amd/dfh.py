@@ -60,6 +60,8 @@ _lock = threading.Lock()
 _SIGNATURES = {
     "df_histogram_device": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                            ctypes.c_void_p]),
+    "df_symbol_device": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
     "df_encode_layout": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint8,
                                         ctypes.c_void_p, ctypes.c_void_p]),
     "df_build_tables": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
@@ -359,6 +361,15 @@ def df_histogram_device(kind: int, src: torch.Tensor, n=None, stream=None) -> to
     return h
 
 
+def df_symbol_device(kind: int, src: torch.Tensor, i: int, stream=None) -> torch.Tensor:
+    """The coded symbol of element i (a device int64 tensor of one element)."""
+    _device_elements(kind, src, None if kind != KIND_U4 else i + 1)
+    out = torch.zeros(1, dtype=torch.int64, device=src.device)
+    _check(lib().df_symbol_device(kind, ctypes.c_void_p(src.data_ptr()), int(i), ctypes.c_void_p(out.data_ptr()),
+                                  _stream_handle(stream, src.device)), "df_symbol_device")
+    return out
+
+
 def df_encode_layout(kind: int, n: int, hist, last_symbol: int, lengths) -> df_info:
     h = np.ascontiguousarray(hist, np.uint64)
     ln = np.ascontiguousarray(lengths, np.uint8)
@@ -428,23 +439,17 @@ def compress_device_batch(kind: int, srcs, max_len: int = MAX_LEN, ns=None, stre
             _check(lib().df_histogram_device(kind, ctypes.c_void_p(t.data_ptr()), n,
                                              ctypes.c_void_p(hists[i].data_ptr()), ctypes.c_void_p(ts.cuda_stream)),
                    "df_histogram_device")
-            if n:   # the element whose symbol ends the stream (uint4: its byte)
-                if kind == KIND_BF16:
-                    lasts[i] = t.view(torch.int16)[n - 1]
-                elif kind == KIND_U8:
-                    lasts[i] = t[n - 1]
-                else:
-                    lasts[i] = t[(n - 1) // 2]
+            if n:   # the symbol of the element that ends the stream
+                _check(lib().df_symbol_device(kind, ctypes.c_void_p(t.data_ptr()), n - 1,
+                                              ctypes.c_void_p(lasts[i].data_ptr()), ctypes.c_void_p(ts.cuda_stream)),
+                       "df_symbol_device")
         back = torch.cat([hists.view(-1), lasts]).cpu().numpy()
 
         def host_part(i):   # codebook, layout and tables of container i
             n = ns[i]
             hist = back[256 * i: 256 * i + 256].view(np.uint64)
-            v = int(back[256 * k + i])
-            last = ((v & 0xFFFF) >> 7) & 0xFF if kind == KIND_BF16 else \
-                (v & 0xFF) if kind == KIND_U8 else ((v & 0xFF) >> (4 * ((n - 1) & 1))) & 0xF
             lengths = df_build_codebook(hist, max_len)
-            lay = df_encode_layout(kind, n, hist, last if n else 0, lengths)
+            lay = df_encode_layout(kind, n, hist, int(back[256 * k + i]), lengths)
             lut, _, dtab = df_build_tables(kind, lengths)
             return lay, lengths, (lut.view(np.uint8), dtab.view(np.uint8))
 
@@ -481,7 +486,10 @@ def compress_device_batch(kind: int, srcs, max_len: int = MAX_LEN, ns=None, stre
     out = []
     for i in range(k):
         infos[i]["max_tile_elems"] = int(mt[i])
-        out.append(DeviceContainer(None, dev, _info=infos[i], _sections=secs[i]))
+        dc = DeviceContainer(None, dev, _info=infos[i], _sections=secs[i])
+        dc.layout = lays[i]   # df_encode_layout's result, for encoding again
+        dc.lengths = lens[i]
+        out.append(dc)
     return out
 
 
