@@ -1,10 +1,12 @@
 """Device-side encoding: the sections the GPU encoder writes must be
-byte-identical to the host encoder's (which the CPU tests pin to the
-oracle's), and decode back to the input on the GPU."""
+byte-identical to the CPU oracle's encoding of the same input (histogram,
+code lengths, stream, gaps, tile offsets, sign|mantissa plane, hierarchical
+tables) and to the host encoder's, and decode back to the input on the GPU."""
 import numpy as np
 import pytest
 
 import lossless_entropy_coded_huffman_amd as dfh
+from decoder_tables import dtab_of
 from lossless_entropy_coded_huffman_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -36,14 +38,38 @@ def device_tensor(torch, dev, kind, a):
     return torch.from_numpy(a).to(dev)
 
 
-def check(torch, dev, kind, a, n):
+def check_against_oracle(orc, dc, kind, a, nn):
+    """The device container against the oracle's own encoding of the same
+    input: histogram -> code lengths -> bit-serial encode -> hierarchical
+    tables, and the decoder-side table from its test-side definition."""
+    o = orc.compress(kind, a, n=nn)
+    assert np.array_equal(dc.info["lengths"], o["lengths"])
+    for k in ("n", "total_bits", "n_threads", "n_tiles", "max_tile_elems", "n_luts"):
+        assert dc.info[k] == o[k], k
+    for name in ("bitstream", "gaps", "tile_out", "sign_mantissa", "lut"):
+        want = o[name]
+        if want is None:   # no sign|mantissa plane for uint8 and uint4
+            assert dc.info["section_bytes"][name] == 0
+            continue
+        want = np.ascontiguousarray(want).view(np.uint8)
+        assert dc.info["section_bytes"][name] == want.size, name
+        assert np.array_equal(dc.sections[name][: want.size].cpu().numpy(), want), name
+    want = dtab_of(kind, o["lengths"], orc.canonical_codes(o["lengths"]))
+    assert np.array_equal(dc.sections["dtab"][: want.size].cpu().numpy(), want)
+
+
+def check(torch, dev, kind, a, n, orc=None):
     nn = n if kind == dfh.KIND_U4 else None
     host = dfh.compress(kind, a, n=nn)
     t = device_tensor(torch, dev, kind, a)
     h_dev = dfh.df_histogram_device(kind, t, nn).cpu().numpy().view(np.uint64)
     assert np.array_equal(h_dev, dfh.df_histogram(kind, a, nn))
+    if orc is not None:
+        assert np.array_equal(h_dev, orc.histogram(kind, a, nn))
     dc = dfh.compress_device(kind, t, n=nn)
     torch.cuda.synchronize()
+    if orc is not None:
+        check_against_oracle(orc, dc, kind, a, nn)
     hi = host.info()
     for k in ("n", "total_bits", "n_threads", "n_tiles", "n_luts", "max_tile_elems"):
         assert dc.info[k] == hi[k], k
@@ -64,27 +90,56 @@ def check(torch, dev, kind, a, n):
 
 @pytest.mark.parametrize("kind", [0, 1, 2])
 @pytest.mark.parametrize("n", SIZES)
-def test_device_encoder_matches_host(torch_dev, kind, n):
+def test_device_encoder_matches_oracle_and_host(torch_dev, orc, kind, n):
     torch, dev = torch_dev
     print("encode", kind, n, flush=True)
-    check(torch, dev, kind, host_input(kind, n, n + 11 * kind), n)
+    check(torch, dev, kind, host_input(kind, n, n + 11 * kind), n, orc)
 
 
-def test_device_encoder_long_codes_and_one_symbol(torch_dev):
+def test_device_encoder_long_codes_and_one_symbol(torch_dev, orc):
     torch, dev = torch_dev
     rng = np.random.default_rng(4)
     t3 = synth.bf16_rne((rng.standard_t(3, 2_000_000) * 0.02 / np.sqrt(3)).astype(np.float32))
-    check(torch, dev, 0, t3, t3.size)
-    check(torch, dev, 1, np.full(70_001, 9, np.uint8), 70_001)
+    check(torch, dev, 0, t3, t3.size, orc)
+    # geometric counts: uint8 and uint4 codes past the decoder tables' index width
+    g = np.minimum(rng.geometric(0.45, 1_000_001) - 1, 255).astype(np.uint8)
+    check(torch, dev, 1, g, g.size, orc)
+    q = np.minimum(rng.geometric(0.55, 1_000_001) - 1, 15).astype(np.uint8)
+    check(torch, dev, 2, synth.pack_u4(q), q.size, orc)
+    check(torch, dev, 1, np.full(70_001, 9, np.uint8), 70_001, orc)
+    check(torch, dev, 2, synth.pack_u4(np.full(70_001, 3, np.uint8)), 70_001, orc)
 
 
-def test_device_encoder_8b_block(torch_dev):
+def test_device_encoder_8b_block(torch_dev, orc):
     torch, dev = torch_dev
     src, _ = synth.bf16_block(0)
-    check(torch, dev, 0, src, src.size)
+    check(torch, dev, 0, src, src.size, orc)
     layers = synth.u4_block(0)
     _, p, n, _ = layers[4]
-    check(torch, dev, 2, p, n)
+    check(torch, dev, 2, p, n, orc)
+    _, q, _ = synth.u8_block(1)[0]
+    check(torch, dev, 1, q, q.size, orc)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_symbol_device(torch_dev, orc, kind):
+    # the coded symbol of single elements, against the oracle's field split
+    # (BF16 exponent), the byte itself (uint8) and the nibble (uint4)
+    torch, dev = torch_dev
+    n = 100_001
+    a = host_input(kind, n, 31 + kind)
+    if kind == dfh.KIND_BF16:
+        a = np.random.default_rng(5).integers(0, 65536, n).astype(np.uint16)   # every exponent
+    t = device_tensor(torch, dev, kind, a)
+    for i in (0, 1, 2, 77, n // 2, n - 2, n - 1):
+        got = int(dfh.df_symbol_device(kind, t, i).item())
+        if kind == dfh.KIND_BF16:
+            want = int(orc.split_bf16(a[i:i + 1])[0][0])
+        elif kind == dfh.KIND_U8:
+            want = int(a[i])
+        else:
+            want = int(a[i // 2] >> (4 * (i % 2))) & 15
+        assert got == want, (kind, i)
 
 
 def test_device_encoder_rejects_misaligned_source(torch_dev):

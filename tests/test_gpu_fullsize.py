@@ -48,11 +48,12 @@ def check_sampled_ranges(torch, orc, c, out, ranges):
         assert np.array_equal(got, ref), (b0, b1)
 
 
-def test_llama3_8b_32_blocks(torch_dev, orc):
+@pytest.mark.parametrize("seed", [0, 1])
+def test_llama3_8b_32_blocks(torch_dev, orc, seed):
     torch, dev = torch_dev
     scratch = None
     for j in range(32):
-        src, _ = synth.bf16_block(0, config=synth.CONFIG_8B_FULL, block=j)
+        src, _ = synth.bf16_block(seed, config=synth.CONFIG_8B_FULL, block=j)
         c = dfh.compress(0, src)
         dc = dfh.to_device(c, dev)
         if scratch is None:
@@ -63,14 +64,15 @@ def test_llama3_8b_32_blocks(torch_dev, orc):
         if j in (0, 31):
             nt = int(c.info()["n_tiles"])
             check_sampled_ranges(torch, orc, c, scratch, [(0, 8), (nt // 2, nt // 2 + 8), (nt - 8, nt)])
-        say("block", j, "ok")
+        say("block", j, "seed", seed, "ok")
         del dc, ref
 
 
-def test_llama31_405b_block_t3(torch_dev, orc):
+@pytest.mark.parametrize("seed", [0, 1])
+def test_llama31_405b_block_t3(torch_dev, orc, seed):
     torch, dev = torch_dev
-    say("405B block: generate")
-    src, _ = synth.bf16_block(0, config=synth.CONFIG_405B, shapes=synth.LLAMA31_405B_BLOCK, dist="t3")
+    say("405B block: generate, seed", seed)
+    src, _ = synth.bf16_block(seed, config=synth.CONFIG_405B, shapes=synth.LLAMA31_405B_BLOCK, dist="t3")
     assert src.size == 3_187_671_040
     say("405B block: compress")
     c = dfh.compress(0, src)
@@ -94,7 +96,7 @@ def test_llama31_405b_block_t3(torch_dev, orc):
         ok = ok and bool(torch.equal(out[lo:hi].view(torch.int16), ref))
     assert ok
     nt = int(inf["n_tiles"])
-    rng = np.random.default_rng(7)
+    rng = np.random.default_rng(7 + seed)
     ranges = [(0, 4), (nt // 2, nt // 2 + 4), (nt - 4, nt)]
     ranges += [(int(b), int(b) + 2) for b in rng.integers(0, nt - 2, 5)]
     say("405B block: oracle ranges")

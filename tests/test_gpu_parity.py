@@ -344,12 +344,13 @@ def test_rejects_bad_arguments(torch_dev):
 
 
 # ------------------------------------------------------------ full-size cases
-def test_llama3_8b_block_bf16(torch_dev, orc):
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_llama3_8b_block_bf16(torch_dev, orc, seed):
     """One Llama-3-8B-shaped block (218,103,808 BF16 weights), one codebook,
     one launch -- the benchmark's workload and launch."""
     torch, dev = torch_dev
-    say("8B block: generate")
-    src, _ = synth.bf16_block(0)
+    say("8B block: generate, seed", seed)
+    src, _ = synth.bf16_block(seed)
     say("8B block: compress")
     c = dfh.compress(0, src)
     inf = c.info()
@@ -368,38 +369,39 @@ def test_llama3_8b_block_bf16(torch_dev, orc):
     assert np.array_equal(got, orc.decode_tiles(oracle_container(c), 16))
 
 
-def test_llama3_8b_block_u8(torch_dev, orc):
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_llama3_8b_block_u8(torch_dev, orc, seed):
     """The EntroLLM-style block: seven per-layer uint8 containers, one batched
-    launch."""
+    launch; every layer against its input and the oracle's decode."""
     torch, dev = torch_dev
-    layers = synth.u8_block(0)
+    layers = synth.u8_block(seed)
     cs = [dfh.compress(1, q) for _, q, _ in layers]
     dcs = [dfh.to_device(c, dev) for c in cs]
     outs = [dc.empty_output() for dc in dcs]
     dfh.df_decompress_batch(dcs, outs)
     torch.cuda.synchronize()
     for (name, q, _), c, o in zip(layers, cs, outs):
-        say("u8 layer", name)
+        say("u8 layer", name, "seed", seed)
         assert torch.equal(o, torch.from_numpy(q).to(dev))
-    got = host_of(outs[4], 1)
-    assert np.array_equal(got, orc.decode_tiles(oracle_container(cs[4]), 16))
+        assert np.array_equal(host_of(o, 1), orc.decode_tiles(oracle_container(c), 16))
 
 
-def test_llama3_8b_block_u4(torch_dev, orc):
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_llama3_8b_block_u4(torch_dev, orc, seed):
     """The 4-bit EntroLLM-style block: seven per-layer uint4 containers, one
-    batched launch, packed outputs."""
+    batched launch, packed outputs; every layer against its input and the
+    oracle's packed decode."""
     torch, dev = torch_dev
-    layers = synth.u4_block(0)
+    layers = synth.u4_block(seed)
     cs = [dfh.compress(dfh.KIND_U4, p, n=n) for _, p, n, _ in layers]
     dcs = [dfh.to_device(c, dev) for c in cs]
     outs = [dc.empty_output() for dc in dcs]
     dfh.df_decompress_batch(dcs, outs)
     torch.cuda.synchronize()
-    for (name, p, n, _), o in zip(layers, outs):
-        say("u4 layer", name)
+    for (name, p, n, _), c, o in zip(layers, cs, outs):
+        say("u4 layer", name, "seed", seed)
         assert torch.equal(o, torch.from_numpy(p).to(dev))
-    got = host_of(outs[4], 2)
-    assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(cs[4]), 16)))
+        assert np.array_equal(host_of(o, 2), orc.pack_u4(orc.decode_tiles(oracle_container(c), 16)))
 
 
 def test_offsets_beyond_2_pow_31(torch_dev):
@@ -529,3 +531,43 @@ def test_bf16_random_sizes_and_distributions(torch_dev, orc):
         else:
             got, err = gpu_decode(torch_dev, dfh.compress(0, src), checked=bool(case & 1))
             assert err == 0 and np.array_equal(got, src)
+
+
+# ------------------------------------------- damaged decoder-side table
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_table_entries_that_consume_no_bits(torch_dev, orc, kind):
+    """Every entry of the decoder-side table replaced from the host by one that
+    claims a code but consumes no bits (the kind of damage a caller-made view
+    with a bad table could bring).  The kernel clears such entries while
+    staging the table, so every code takes the hierarchical tables (intact
+    here): the output is still the input, and a checked launch reports
+    DF_DEVERR_CODE."""
+    torch, dev = torch_dev
+    n = 3_000_001
+    if kind == 0:
+        src = bf16_normal(n, 41)
+        c = dfh.compress(0, src)
+    elif kind == 1:
+        src = u8_normal(n, 42, True)
+        c = dfh.compress(1, src)
+    else:
+        q = u4_symbols(n, 43)
+        src = synth.pack_u4(q)
+        c = dfh.compress(2, src, n=n)
+    dc = dfh.to_device(c, dev)
+    tab = dc.sections["dtab"]
+    if kind == 1:   # uint8: 8192 u32 pair entries (count 1, 0 bits), lengths left
+        tab[: 4 * 8192].view(torch.int32).fill_(1 << 24)
+    else:           # u64 entries: high word count 1, 0 bits; low word symbols
+        tab[: 8 * 4096].view(torch.int32).view(-1, 2)[:, 1].fill_(1 << 24)
+    for checked in (False, True):
+        out = dc.empty_output()
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        if checked:
+            dfh.df_decompress_checked(dc, out, err)
+        else:
+            dfh.df_decompress(dc, out)
+        torch.cuda.synchronize()
+        say("damaged table", kind, "checked", checked, "err", int(err.item()))
+        assert np.array_equal(host_of(out, kind), src)
+        assert int(err.item()) == (dfh.DEVERR_CODE if checked else 0)
