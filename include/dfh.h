@@ -119,7 +119,8 @@ typedef enum {
 
 /* Device error bits written by df_decompress_checked. */
 #define DF_DEVERR_COUNT 1u  /* a tile (uint8: a pair of tiles) decodes to a different count than tile_out says */
-#define DF_DEVERR_CODE 2u   /* a stream prefix matches no code                      */
+#define DF_DEVERR_CODE 2u   /* a stream prefix matches no code, or a decode table
+                              entry claims codes but consumes no bits            */
 
 typedef struct {
   df_kind kind;
@@ -225,10 +226,11 @@ typedef struct {
  * Scheduling: a BF16 container of more than three steps of tiles (three
  * times the launch's tile groups) is decoded with tiles handed out by
  * device-side counters that the library keeps in its code object (no
- * allocation; each launch leaves its counters zero).  Up to 3584 such jobs
- * may be in flight on one device at once; a launch under stream capture
- * takes one of 512 counter slots reserved for graphs for the life of the
- * process, after which captured launches use the static tile order.  The
+ * allocation).  Each running dispatch claims its own counter slot on the
+ * device, keyed by its dispatch packet, and frees it clean when its last
+ * tile has been handed out, so no state carries from one launch to the
+ * next and launches running at once (several streams, several instances of
+ * one captured graph) never share counters.  The
  * decoded bytes do not depend on the schedule. */
 df_status df_decompress(const df_device_view *v, void *dst, hipStream_t stream);
 
@@ -255,7 +257,8 @@ df_status df_decompress_batch(const df_device_view *views, void *const *dsts, ui
  * conversion of a checkpoint; the pages encode offline and describe no
  * encoder kernel, so this part is this library's own).  The sections it
  * writes are byte-identical to df_encode's.  Steps:
- *   1. df_histogram_device, then copy the 256 counts to the host;
+ *   1. df_histogram_device and df_symbol_device (the last element's
+ *      symbol), then copy the 256 counts and the symbol to the host;
  *   2. df_build_codebook on the host;
  *   3. df_encode_layout for the sizes, df_build_tables for LUT and DTAB;
  *   4. allocate the device sections and df_encode_workspace_bytes(n) bytes
@@ -268,6 +271,14 @@ df_status df_decompress_batch(const df_device_view *views, void *const *dsts, ui
  * pointer or a bad kind. */
 df_status df_histogram_device(df_kind kind, const void *d_src, uint64_t n, uint64_t *d_hist,
                               hipStream_t stream);
+
+/* The coded symbol of device element i (the BF16 exponent byte
+ * (u >> 7) & 0xFF, the uint8 value, or the uint4 nibble; layout as for
+ * df_histogram), written to *d_sym as one device uint64 (8-byte aligned).
+ * With i = n - 1 it is the last_symbol df_encode_layout takes.  i must lie
+ * inside the source; DF_ERR_ARG on a null or misaligned pointer or a bad
+ * kind. */
+df_status df_symbol_device(df_kind kind, const void *d_src, uint64_t i, uint64_t *d_sym, hipStream_t stream);
 
 /* Header scalars and section sizes of the container df_encode would build
  * for n elements with this histogram and these lengths, whose last element

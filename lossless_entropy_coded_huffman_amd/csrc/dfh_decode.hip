@@ -109,22 +109,104 @@ struct Job {
   void *dst;
   uint64_t n, total_bits, n_threads, n_tiles;
   uint32_t n_luts, wg_begin, wg_count, max_tile_elems;
-  uint32_t ticket;  // tile counter slot of the dynamic schedule, or kNoTicket
+  uint32_t ticket;  // the dynamic schedule's first-choice counter slot, or kNoTicket
   uint32_t pad;
 };
 
-// Tile counters of the dynamic schedule (BF16).  A slot per launch in flight
-// (per job of a batched launch), of kParts counters on separate 128-byte
-// lines: atomics on one address serialize at about 11 ns each on MI355X,
-// atomics on separate lines proceed in parallel.  Zero when the code object
-// is loaded; the launch that uses a counter leaves it zero again (the grab
-// that takes its last value stores zero), so no launch clears memory.
+// Tile counters of the dynamic schedule (BF16).  Each dynamically scheduled
+// job of a running dispatch owns one slot of kParts counters on separate
+// 128-byte lines (atomics on one address serialize at about 11 ns each on
+// MI355X, atomics on separate lines proceed in parallel), plus a line with
+// the owner's key and a count of finished counters.  A dispatch claims its
+// slot on the device and frees it when its last grab has been served, so no
+// state passes from one launch to another and concurrent launches never
+// share counters, whatever the host does (graph instances replayed on
+// several streams included):
+//   - the key is the address of the dispatch's AQL packet (the same for all
+//     its workgroups, different for any two dispatches running at once)
+//     with the job's index in its six low bits, which a 64-byte packet
+//     address leaves zero;
+//   - the job's first workgroup claims the first free slot from the host's
+//     hint on (compare-and-swap of the owner word from zero to the key),
+//     within kWindow slots, waiting for one to free up if all are held;
+//   - its other workgroups look for the key in the same slots;
+//   - the grab that takes a counter's last value counts that counter as
+//     finished; the last counter to finish clears the counters, then frees
+//     the slot (a release store of zero to the owner word).
+// Every slot is zero when the code object is loaded and zero again when its
+// dispatch ends, so no launch clears memory.  All slot accesses are
+// system-scope atomics, performed at one coherence point.  A workgroup that
+// cannot claim or find its slot within kSpinLimit polls (never seen: it
+// would take more than kWindow decodes running at once next to the hint)
+// decodes every dynamically dealt unit itself, which covers the job
+// whatever its other workgroups do (the writes are identical).
 constexpr uint32_t kParts = 8;
 constexpr uint32_t kCounterStride = 32;  // u32 words: 128 bytes
+constexpr uint32_t kSlotWords = (kParts + 1) * kCounterStride;
 constexpr uint32_t kTicketSlots = 4096;
-constexpr uint32_t kCaptureSlots = 512;  // the top slots: launches under stream capture
+constexpr uint32_t kWindow = 16;
+constexpr uint32_t kSpinLimit = 1u << 16;
 constexpr uint32_t kNoTicket = 0xFFFFFFFFu;
-__device__ uint32_t g_tickets[kTicketSlots * kParts * kCounterStride];
+__device__ uint32_t g_slots[kTicketSlots * kSlotWords];
+
+__device__ __forceinline__ uint64_t *slot_owner(uint32_t s) { return (uint64_t *)(g_slots + (size_t)s * kSlotWords); }
+__device__ __forceinline__ uint32_t *slot_done(uint32_t s) { return g_slots + (size_t)s * kSlotWords + 2; }
+__device__ __forceinline__ uint32_t *slot_counter(uint32_t s, uint32_t c) {
+  return g_slots + (size_t)s * kSlotWords + (c + 1) * kCounterStride;
+}
+__device__ __forceinline__ uint32_t window_slot(uint32_t hint, uint32_t i) { return (hint + i % kWindow) % kTicketSlots; }
+
+// The first workgroup's claim, given the result of the compare-and-swap it
+// made at the hint: the hint, or the first slot of the window it can claim.
+__device__ uint32_t claim_slot(uint32_t hint, uint64_t key, uint64_t at_hint) {
+  if (at_hint == 0) return hint;
+  for (uint32_t k = 1; k < kSpinLimit; k++) {
+    if (k % kWindow == 0) __builtin_amdgcn_s_sleep(8);  // every slot held: wait for one
+    uint64_t expect = 0;
+    if (__hip_atomic_compare_exchange_strong(slot_owner(window_slot(hint, k)), &expect, key, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+      return window_slot(hint, k);
+  }
+  return kNoTicket;
+}
+
+// Another workgroup's search for the slot its first workgroup claimed: a
+// slot held by another key is passed (the claim lies further on); at a free
+// slot the claim is awaited, and after a while the search starts over at
+// the hint (a slot passed as held may have been freed and then claimed).
+__device__ uint32_t find_slot(uint32_t hint, uint64_t key) {
+  uint32_t i = 0, waits = 0;
+  for (uint32_t k = 0; k < kSpinLimit; k++) {
+    const uint32_t s = window_slot(hint, i);
+    const uint64_t v = __hip_atomic_load(slot_owner(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (v == key) return s;
+    if (v != 0) {
+      i++;
+      waits = 0;
+      continue;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    if (++waits == 64) i = waits = 0;
+  }
+  return kNoTicket;
+}
+
+// Counter c's last grab of the dispatch has been served.  The last of the
+// slot's `parts` counters to finish clears them, then frees the slot.  The
+// clears must be done before the owner word reads free: system-scope stores
+// are written through to the coherence point and count in vmcnt until it
+// acknowledges them, so a vmcnt(0) wait between the two suffices (a release
+// store would also write back the whole L2, which the decoder's output
+// fills).
+__device__ void counter_finished(uint32_t s, uint32_t parts) {
+  if (__hip_atomic_fetch_add(slot_done(s), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) + 1 < parts) return;
+  for (uint32_t c = 0; c < parts; c++) __hip_atomic_store(slot_counter(s, c), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(slot_done(s), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_store(slot_owner(s), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 // The kinds that use it: with the BF16 block the slowest CUs set the end of a
 // static schedule (measured 4.3% faster with it); the uint8 and uint4
 // kernels measured 1.5% and 11% slower with it compiled in.
@@ -610,6 +692,13 @@ void decode_kernel(const Batch batch) {
   const uint32_t buf = kTabBytes<KIND> + batch.lut_bytes + grp * out_bytes;  // LDS byte offset
   lds_u32 *wsum = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes);
 
+  // dynamic schedule (BF16): the job's first workgroup claims a counter
+  // slot, the others look for its key (requested behind the table loads
+  // below, read after the staging)
+  const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
+  const bool lead = wg == jb.wg_begin;
+  const uint64_t key = (uint64_t)(uintptr_t)__builtin_amdgcn_dispatch_ptr() | (j + 1);
+  uint64_t at_hint = 0;
   {  // stage the tables once per workgroup: the first four 16-byte words per
      // lane (all a 1024-lane workgroup needs for up to 64 levels) with every
      // load issued before any write, the rest one by one
@@ -624,6 +713,16 @@ void decode_kernel(const Batch batch) {
     const v4u t1 = i1 < total ? (i1 < kTabWords ? dsrc[i1] : lsrc[i1]) : z;
     const v4u t2 = i2 < total ? (i2 < kTabWords ? dsrc[i2] : lsrc[i2]) : z;
     const v4u t3 = i3 < total ? (i3 < kTabWords ? dsrc[i3] : lsrc[i3]) : z;
+    if (dyn && tid == 0) {
+      if (lead) {
+        uint64_t expect = 0;
+        __hip_atomic_compare_exchange_strong(slot_owner(jb.ticket), &expect, key, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        at_hint = expect;
+      } else {
+        at_hint = __hip_atomic_load(slot_owner(jb.ticket), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
     if (i0 < total) dl[i0] = i0 < kTabWords ? clean_tab<KIND, CHECKED>(t0, i0, batch.err) : t0;
     if (i1 < total) dl[i1] = i1 < kTabWords ? clean_tab<KIND, CHECKED>(t1, i1, batch.err) : t1;
     if (i2 < total) dl[i2] = i2 < kTabWords ? clean_tab<KIND, CHECKED>(t2, i2, batch.err) : t2;
@@ -653,11 +752,14 @@ void decode_kernel(const Batch batch) {
   const uint32_t n_spans = (n_tiles + C - 1) / C;
   const uint32_t step = jb.wg_count * groups;
   uint32_t base = (wg - jb.wg_begin) * groups;
-  const bool dyn = kDynamic<KIND> && jb.ticket != kNoTicket;
   uint32_t base_nxt = base + step;  // the workgroup's first tile next step
-  // the one lane that grabs (thread 0) keeps the counter's constants in LDS:
-  // word 0 the published first tile (0xFFFFFFFF: none), 2..3 the counter's
-  // address, 4 the first unit, 5 the unit stride, 6 the counter's last value
+  // the one lane that grabs (thread 0) keeps the schedule's state in LDS:
+  // word 0 the published first tile (0xFFFFFFFF: none), 1 the slot
+  // (kNoTicket: not known yet), 2..3 the counter's address (0: the
+  // workgroup deals units to itself, no slot found), 4 the first unit, 5 the
+  // unit stride, 6 the counter's last value, 7 the counter c, plus 16 once
+  // its last value has been taken, plus 32 when the workgroup deals units to
+  // itself, 8..9 the key, 10 the number of counters
   lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 16 * groups);
   if (dyn && tid == 0) {
     const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
@@ -668,15 +770,31 @@ void decode_kernel(const Batch batch) {
     const uint32_t units = (n_spans + groups - 1) / groups;
     const uint32_t first = 3 * nwg + c;
     const uint32_t vc = units > first ? (units - first + parts - 1) / parts : 0u;
-    const uint64_t cp = (uint64_t)(uintptr_t)(g_tickets + ((size_t)jb.ticket * kParts + c) * kCounterStride);
-    nx_lds[2] = (uint32_t)cp;
-    nx_lds[3] = (uint32_t)(cp >> 32);
+    // the lead's claim is settled here; another workgroup that did not see
+    // its key at the hint yet searches at its first grab
+    const uint32_t sl = lead ? claim_slot(jb.ticket, key, at_hint) : at_hint == key ? jb.ticket : kNoTicket;
+    nx_lds[1] = sl;
     nx_lds[4] = first;
     nx_lds[5] = parts;
     nx_lds[6] = (uint32_t)(vc + wc - 1);
+    nx_lds[7] = c;
+    nx_lds[8] = (uint32_t)key;
+    nx_lds[9] = (uint32_t)(key >> 32);
+    nx_lds[10] = parts;
+    const uint64_t cp = sl == kNoTicket ? 0 : (uint64_t)(uintptr_t)slot_counter(sl, c);
+    nx_lds[2] = (uint32_t)cp;
+    nx_lds[3] = (uint32_t)(cp >> 32);
+    if (lead && sl == kNoTicket) {  // no slot: deal every unit to itself
+      nx_lds[4] = 3 * nwg;
+      nx_lds[5] = 1;
+      nx_lds[6] = 0xFFFFFFFFu;
+      nx_lds[7] = 32;
+    }
   }
   bool first_step = true, grabbed = false;
-  uint32_t tk = 0;  // the grab in flight (lane 0 of the workgroup)
+  // the grab in flight (lane 0 of the workgroup); a workgroup that deals
+  // units to itself counts its grabs here, so the first gives unit 0
+  uint32_t tk = 0xFFFFFFFFu;
   ChunkRegs nxt = load_chunk<KIND>(jb, base + grp, lane);
   // the next span's first and last output index, one step ahead
   k_u64 *tout = (k_u64 *)jb.tile_out;
@@ -805,8 +923,7 @@ void decode_kernel(const Batch batch) {
     if (dyn && tid == 0) {  // last step's grab, for the workgroup: its first tile
       uint32_t pub = 0xFFFFFFFFu;  // no tile: past any span index
       if (grabbed) {
-        uint32_t *ctr = (uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]);
-        if (tk == nx_lds[6]) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (tk == nx_lds[6]) nx_lds[7] |= 16;  // the counter's last value: freed at exit
         // a grab past the last unit gives a tile past the end; clamp so the
         // product cannot wrap into the span range
         const uint64_t t = (uint64_t)groups * (nx_lds[4] + (uint64_t)nx_lds[5] * tk);
@@ -823,9 +940,24 @@ void decode_kernel(const Batch batch) {
       if (dyn && !first_step) base_nxt2 = __builtin_amdgcn_readfirstlane(nx_lds[0]);
       first_step = false;
       grabbed = dyn && base_nxt2 < n_spans;
-      if (grabbed && tid == 0)
-        tk = __hip_atomic_fetch_add((uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]), 1u,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (grabbed && tid == 0) {
+        if (nx_lds[1] == kNoTicket && !(nx_lds[7] & 32)) {  // slot not known yet (first grab)
+          const uint32_t sl = find_slot(jb.ticket, ((uint64_t)nx_lds[9] << 32) | nx_lds[8]);
+          nx_lds[1] = sl;
+          if (sl == kNoTicket) {  // no slot found: deal every unit to itself
+            nx_lds[4] = 3 * jb.wg_count;
+            nx_lds[5] = 1;
+            nx_lds[6] = 0xFFFFFFFFu;
+            nx_lds[7] = 32;
+          } else {
+            const uint64_t cp = (uint64_t)(uintptr_t)slot_counter(sl, nx_lds[7] & 15);
+            nx_lds[2] = (uint32_t)cp;
+            nx_lds[3] = (uint32_t)(cp >> 32);
+          }
+        }
+        uint32_t *ctr = (uint32_t *)(uintptr_t)(((uint64_t)nx_lds[3] << 32) | nx_lds[2]);
+        tk = ctr ? __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : tk + 1;
+      }
     }
     const lds_u32 *ws = wsum + 4 * grp;
     const uint32_t s0 = ws[0], s1 = ws[1], s2 = ws[2], s3 = ws[3];
@@ -895,6 +1027,9 @@ void decode_kernel(const Batch batch) {
       base += step;
     }
   }
+  // a workgroup that took its counter's last value counts it finished (the
+  // last counter of the slot to finish frees the slot)
+  if (dyn && tid == 0 && (nx_lds[7] & 16) && nx_lds[1] != kNoTicket) counter_finished(nx_lds[1], nx_lds[10]);
   // the last tile of this group
   if (have_prev) {
     uint2 smv[kPrefetch];
@@ -980,26 +1115,11 @@ uint32_t out_bytes_for(df_kind kind, uint32_t max_tile_elems) {
   return ((max_tile_elems + 15 + kSlack + 15) & ~15u) + 16;
 }
 
-// A tile counter slot for one job of a launch.  Launches under stream
-// capture take slots of their own for good (a captured graph replays its
-// slot, and replays of one graph run one after another), kCaptureSlots over
-// the process, then decode with the static schedule; other launches cycle
-// through the rest, which is safe while fewer than kTicketSlots -
-// kCaptureSlots dynamically scheduled jobs are in flight on one device.
-std::atomic<uint64_t> g_eager_slots{0};
-std::atomic<uint32_t> g_capture_slots{0};
-uint32_t ticket_slot(hipStream_t stream) {
-  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
-    (void)hipGetLastError();
-    return kNoTicket;
-  }
-  if (st != hipStreamCaptureStatusNone) {
-    const uint32_t c = g_capture_slots.fetch_add(1);
-    return c < kCaptureSlots ? kTicketSlots - kCaptureSlots + c : kNoTicket;
-  }
-  return (uint32_t)(g_eager_slots.fetch_add(1) % (kTicketSlots - kCaptureSlots));
-}
+// The first-choice counter slot of a dynamically scheduled job.  Launches
+// take hints in turn, so that jobs in flight at once usually claim their
+// hinted slot at the first try; the device settles the claim either way.
+std::atomic<uint32_t> g_hint{0};
+uint32_t ticket_slot() { return g_hint.fetch_add(1) % kTicketSlots; }
 
 df_status launch(const df_device_view *views, void *const *dsts, uint32_t count, uint32_t *err,
                  bool checked, hipStream_t stream) {
@@ -1044,7 +1164,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
       const size_t need = (size_t)(kind == DF_KIND_U8 ? kTabBytes<DF_KIND_U8> : kDtabBytes) + lut_bytes +
-                          (size_t)g * out_bytes + 16 * g + 32;
+                          (size_t)g * out_bytes + 16 * g + 64;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
@@ -1086,7 +1206,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
       jb.wg_count = (uint32_t)share;
       jb.ticket = kNoTicket;
       if (kind == DF_KIND_BF16 && v.n_tiles > 3 * share * groups && v.n_tiles < (1ull << 31))
-        jb.ticket = ticket_slot(stream);
+        jb.ticket = ticket_slot();
       wg += (uint32_t)share;
     }
     b.count = nj;

@@ -1,9 +1,11 @@
 """The BF16 kernel's dynamic tile schedule: a container with more than three
-steps of tiles is decoded with tiles handed out by device counters, which
-each launch leaves at zero for the next launch that uses the same slot.
-These tests decode such containers bit-exactly past a full cycle of counter
-slots, on two streams at once, and from a replayed HIP graph.  Every call
-goes through the C ABI."""
+steps of tiles is decoded with tiles handed out by device counters.  Each
+dispatch claims a counter slot on the device (keyed by its own dispatch
+packet), starting at a slot the host hints, and frees it clean when its last
+grab is served.  These tests decode such containers bit-exactly past a full
+cycle of hints, on two streams at once, from a replayed HIP graph, and from
+several instances of one captured graph (one frozen hint) launched on
+several streams at once.  Every call goes through the C ABI."""
 import sys
 
 import numpy as np
@@ -14,8 +16,8 @@ from lossless_entropy_coded_huffman_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-# slots launches cycle through outside stream capture (4096 - 512)
-EAGER_SLOTS = 3584
+# counter slots; launches take them as hints in turn
+SLOTS = 4096
 
 
 def say(*a):
@@ -45,13 +47,13 @@ def block(torch_dev):
 
 
 def test_decodes_past_a_cycle_of_counter_slots(torch_dev, block):
-    # every launch takes the next slot; past EAGER_SLOTS launches the slots
-    # come round again, so each must have been left at zero
+    # every launch is hinted the next slot; past SLOTS launches the hints
+    # come round again, so each slot must have been freed clean
     torch, dev = torch_dev
     dc, ref = block
     outs = [dc.empty_output() for _ in range(2)]
     bad = torch.zeros(1, dtype=torch.int64, device=dev)
-    n = EAGER_SLOTS + 200
+    n = SLOTS + 200
     say("dynamic schedule:", n, "launches")
     for k in range(n):
         o = outs[k % 2]
@@ -82,7 +84,8 @@ def test_two_streams_at_once(torch_dev, block):
 
 
 def test_graph_replays(torch_dev, block):
-    # a captured launch keeps its slot; every replay must leave it at zero
+    # a captured launch keeps its hint; every replay claims a slot and must
+    # free it clean
     torch, dev = torch_dev
     dc, ref = block
     out = dc.empty_output()
@@ -144,3 +147,116 @@ def test_batched_large_jobs(torch_dev, block):
         torch.cuda.synchronize()
         for k, o in enumerate(outs):
             assert torch.equal(o.view(torch.int16), ref), (rep, k)
+
+
+class _HipGraphs:
+    """Stream capture and graph instances through the HIP runtime that torch
+    has loaded (torch's CUDAGraph instantiates a capture only once)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.L = ctypes.CDLL("libamdhip64.so")
+        P = ctypes.c_void_p
+        for name, args in (("hipStreamBeginCapture", [P, ctypes.c_int]),
+                           ("hipStreamEndCapture", [P, ctypes.POINTER(P)]),
+                           ("hipGraphInstantiate", [ctypes.POINTER(P), P, P, P, ctypes.c_size_t]),
+                           ("hipGraphLaunch", [P, P]), ("hipGraphExecDestroy", [P]),
+                           ("hipGraphDestroy", [P])):
+            getattr(self.L, name).argtypes = args
+            getattr(self.L, name).restype = ctypes.c_int
+
+    def capture(self, stream, fn):
+        ct = self.ct
+        assert self.L.hipStreamBeginCapture(ct.c_void_p(stream.cuda_stream), 2) == 0   # relaxed mode
+        fn()
+        g = ct.c_void_p()
+        assert self.L.hipStreamEndCapture(ct.c_void_p(stream.cuda_stream), ct.byref(g)) == 0
+        return g
+
+    def instantiate(self, g):
+        e = self.ct.c_void_p()
+        assert self.L.hipGraphInstantiate(self.ct.byref(e), g, None, None, 0) == 0
+        return e
+
+    def launch(self, e, stream):
+        assert self.L.hipGraphLaunch(e, self.ct.c_void_p(stream.cuda_stream)) == 0
+
+
+def test_instances_of_one_graph_on_several_streams(torch_dev, block):
+    # one captured decode (one frozen hint, one destination) instantiated
+    # three times, the instances launched on three streams at once: each
+    # dispatch must claim its own slot (two find the hinted one taken) and
+    # free it clean.  Afterwards each instance replayed alone into a cleared
+    # destination, and eager decodes, must be exact: a slot left dirty would
+    # make them skip tiles.
+    torch, dev = torch_dev
+    dc, ref = block
+    hg = _HipGraphs()
+    out = dc.empty_output()
+    eager = dc.empty_output()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    g = hg.capture(cap, lambda: dfh.df_decompress(dc, out, cap))
+    execs = [hg.instantiate(g) for _ in range(3)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(3)]
+    try:
+        for rnd in range(8):
+            out.view(torch.int16).fill_(0)
+            torch.cuda.synchronize()
+            for e, st in zip(execs, streams):
+                hg.launch(e, st)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref), rnd
+            for k, (e, st) in enumerate(zip(execs, streams)):
+                out.view(torch.int16).fill_(0)
+                torch.cuda.synchronize()
+                hg.launch(e, st)
+                torch.cuda.synchronize()
+                assert torch.equal(out.view(torch.int16), ref), (rnd, k)
+            eager.view(torch.int16).fill_(0)
+            dfh.df_decompress(dc, eager)
+            torch.cuda.synchronize()
+            assert torch.equal(eager.view(torch.int16), ref), rnd
+        say("graph instances: 8 rounds of 3 concurrent launches exact")
+    finally:
+        torch.cuda.synchronize()
+        for e in execs:
+            hg.L.hipGraphExecDestroy(e)
+        hg.L.hipGraphDestroy(g)
+
+
+def test_graph_instances_next_to_eager_launches(torch_dev, block):
+    # two instances of one graph on two streams while eager decodes of the
+    # same container run on a third, into separate buffers, several rounds
+    torch, dev = torch_dev
+    dc, ref = block
+    hg = _HipGraphs()
+    gout = dc.empty_output()
+    eouts = [dc.empty_output() for _ in range(3)]
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    g = hg.capture(cap, lambda: dfh.df_decompress(dc, gout, cap))
+    execs = [hg.instantiate(g) for _ in range(2)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(3)]
+    try:
+        for rnd in range(6):
+            gout.view(torch.int16).fill_(0)
+            for o in eouts:
+                o.view(torch.int16).fill_(0)
+            torch.cuda.synchronize()
+            hg.launch(execs[0], streams[0])
+            for o in eouts:
+                dfh.df_decompress(dc, o, streams[2])
+            hg.launch(execs[1], streams[1])
+            torch.cuda.synchronize()
+            assert torch.equal(gout.view(torch.int16), ref), rnd
+            for k, o in enumerate(eouts):
+                assert torch.equal(o.view(torch.int16), ref), (rnd, k)
+    finally:
+        torch.cuda.synchronize()
+        for e in execs:
+            hg.L.hipGraphExecDestroy(e)
+        hg.L.hipGraphDestroy(g)
