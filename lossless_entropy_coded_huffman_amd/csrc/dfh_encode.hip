@@ -431,17 +431,20 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
   }
   const uint64_t n_tiles = layout->n_tiles;
   hipLaunchKernelGGL(fill_zero, dim3(1), dim3(32), 0, stream, d_max_tile, (uint64_t)1);
+  // the stream and gap sections are ORed into, so they start zero; their
+  // padding (the whole section when n == 0) stays zero
+  const uint64_t zb = layout->section_bytes[DF_SEC_BITSTREAM] / 4, zg = layout->section_bytes[DF_SEC_GAPS] / 4;
+  if (d_bitstream && zb) hipLaunchKernelGGL(fill_zero, dim3(1024), dim3(256), 0, stream, (uint32_t *)d_bitstream, zb);
+  if (d_gaps && zg) hipLaunchKernelGGL(fill_zero, dim3(64), dim3(256), 0, stream, (uint32_t *)d_gaps, zg);
+  if (kind == DF_KIND_BF16 && d_sign_mantissa) {  // the padding past n
+    const uint64_t pad0 = n & ~(uint64_t)63, words = (layout->section_bytes[DF_SEC_SIGN_MANTISSA] - pad0) / 4;
+    if (words)
+      hipLaunchKernelGGL(fill_zero, dim3(1), dim3(64), 0, stream, (uint32_t *)(d_sign_mantissa + pad0), words);
+  }
   if (n == 0) {
     hipLaunchKernelGGL(enc_finish, dim3(1), dim3(64), 0, stream, d_tile_out, (uint64_t)0, (uint64_t)0,
                        d_max_tile);
     return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
-  }
-  const uint64_t zb = layout->section_bytes[DF_SEC_BITSTREAM] / 4, zg = layout->section_bytes[DF_SEC_GAPS] / 4;
-  hipLaunchKernelGGL(fill_zero, dim3(1024), dim3(256), 0, stream, (uint32_t *)d_bitstream, zb);
-  hipLaunchKernelGGL(fill_zero, dim3(64), dim3(256), 0, stream, (uint32_t *)d_gaps, zg);
-  if (kind == DF_KIND_BF16) {  // the padding past n
-    const uint64_t pad0 = n & ~(uint64_t)63, words = (layout->section_bytes[DF_SEC_SIGN_MANTISSA] - pad0) / 4;
-    hipLaunchKernelGGL(fill_zero, dim3(1), dim3(64), 0, stream, (uint32_t *)(d_sign_mantissa + pad0), words);
   }
   const uint64_t nb = blocks_for(n);
   if (nb > 0xFFFFFFFFull) return DF_ERR_ARG;

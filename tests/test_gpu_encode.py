@@ -181,3 +181,28 @@ def test_device_encoder_batch_on_a_side_stream(torch_dev, kind):
             want = a.view(np.int16) if kind == dfh.KIND_BF16 else a
             got = out.view(torch.int16) if kind == dfh.KIND_BF16 else out
             assert torch.equal(got, torch.from_numpy(want).to(dev))
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+@pytest.mark.parametrize("n", [0, 1, 65, 4097])
+def test_device_encoder_writes_every_section_byte(torch_dev, orc, kind, n):
+    # sections handed in full of a byte pattern come out equal to the
+    # oracle's, padding included (an empty input's stream and gap sections
+    # are all padding)
+    torch, dev = torch_dev
+    a = host_input(kind, n, 900 + n)
+    t = device_tensor(torch, dev, kind, a)
+    nn = n if kind == dfh.KIND_U4 else None
+    dc = dfh.compress_device(kind, t, n=nn)
+    sec = {name: torch.full_like(dc.sections[name], 0xA5) for name in ("bitstream", "gaps", "tile_out", "sign_mantissa")}
+    ws = torch.empty(max(dfh.df_encode_workspace_bytes(n), 16), dtype=torch.uint8, device=dev)
+    mt = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    dfh.df_encode_device(kind, t, n, dc.lengths, dc.layout, sec, ws, mt)
+    torch.cuda.synchronize()
+    o = orc.compress(kind, a, n=nn)
+    for name in sec:
+        if o[name] is None:
+            continue
+        want = np.ascontiguousarray(o[name]).view(np.uint8)
+        assert np.array_equal(sec[name][: want.size].cpu().numpy(), want), name
+    assert int(mt.item()) == o["max_tile_elems"]
