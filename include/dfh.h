@@ -116,6 +116,7 @@ typedef enum {
 #define DF_DTAB_BITS_U8 13      /* index width of the uint8 pair table        */
 #define DF_DTAB_BYTES_U8 (4 * 8192 + 256) /* uint8 DTAB: pair table + lengths */
 #define DF_MAX_BATCH 16         /* containers per df_decompress_batch launch  */
+#define DF_ENCODE_SCRATCH_BYTES (16u << 20) /* df_encode_device_noalloc's workspace */
 
 /* Device error bits written by df_decompress_checked. */
 #define DF_DEVERR_COUNT 1u  /* a tile (uint8: a pair of tiles) decodes to a different count than tile_out says */
@@ -308,6 +309,24 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
                            const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
                            uint64_t *d_tile_out, uint8_t *d_sign_mantissa, void *d_workspace,
                            uint32_t *d_max_tile, hipStream_t stream);
+
+/* df_encode_device for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as df_encode_device
+ * without d_workspace: the workspace is a DF_ENCODE_SCRATCH_BYTES array in
+ * the library's code object (one per device, held until the process ends;
+ * its address is taken once per device on the first call there).  The call
+ * allocates nothing.  n is limited to df_encode_workspace_bytes(n) <=
+ * DF_ENCODE_SCRATCH_BYTES (about 4.29e9 elements); a larger n gives
+ * DF_ERR_ARG before anything is enqueued.  Every call on one device uses
+ * the same array, and the encode writes every workspace word it reads, so
+ * nothing carries over from the previous call; calls that overlap on one
+ * device (different streams, or graph instances in flight together) race
+ * on it and must be ordered by the caller. */
+df_status df_encode_device_noalloc(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                                   const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
+                                   uint64_t *d_tile_out, uint8_t *d_sign_mantissa, uint32_t *d_max_tile,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

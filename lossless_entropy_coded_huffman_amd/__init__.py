@@ -7,8 +7,9 @@ kernels; both sit behind the C ABI in include/dfh.h, which ``dfh`` binds
 with the same names.  ``synth`` draws the seeded synthetic workloads.
 """
 from .dfh import (  # noqa: F401
-    KIND_BF16, KIND_U4, KIND_U8, MAX_LEN, SECTION_NAMES, DEVERR_CODE, DEVERR_COUNT, DFError, Container,
-    DeviceContainer, compress, compress_device, compress_device_batch, df_build_codebook, df_build_tables, df_encode_device,
+    KIND_BF16, KIND_U4, KIND_U8, MAX_LEN, SECTION_NAMES, DEVERR_CODE, DEVERR_COUNT, ENCODE_SCRATCH_BYTES, DFError,
+    Container,
+    DeviceContainer, compress, compress_device, compress_device_batch, df_build_codebook, df_build_tables, df_encode_device, df_encode_device_noalloc,
     df_encode_layout, df_encode_workspace_bytes, df_histogram_device, df_symbol_device, df_container_free,
     df_container_info,
     df_container_load, df_container_save, df_container_section, df_container_validate,

@@ -24,8 +24,16 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "dfh.h"
+
+// Workspace of df_encode_device_noalloc, in the library's code object: each
+// device the library runs on holds its own copy until the process ends.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in for the symbol); it takes each device's address once with
+// hipGetSymbolAddress and passes that to the kernels.
+static __device__ __align__(256) uint8_t scratch[DF_ENCODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -390,10 +398,64 @@ df_status df_symbol_device(df_kind kind, const void *d_src, uint64_t i, uint64_t
   return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The device address of `scratch` on each device, taken once per device.
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+df_status scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DF_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DF_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DF_OK;
+}
+
+df_status encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                        const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps, uint64_t *d_tile_out,
+                        uint8_t *d_sign_mantissa, void *d_workspace, uint32_t *d_max_tile, hipStream_t stream);
+
+}  // namespace
+
+extern "C" {
+
 df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
                            const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
                            uint64_t *d_tile_out, uint8_t *d_sign_mantissa, void *d_workspace,
                            uint32_t *d_max_tile, hipStream_t stream) {
+  if (n && (!d_workspace || ((uintptr_t)d_workspace & 15))) return DF_ERR_ARG;
+  return encode_device(kind, d_src, n, lengths, layout, d_bitstream, d_gaps, d_tile_out, d_sign_mantissa,
+                       d_workspace, d_max_tile, stream);
+}
+
+df_status df_encode_device_noalloc(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                                   const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps,
+                                   uint64_t *d_tile_out, uint8_t *d_sign_mantissa, uint32_t *d_max_tile,
+                                   hipStream_t stream) {
+  if (df_encode_workspace_bytes(n) > DF_ENCODE_SCRATCH_BYTES) return DF_ERR_ARG;
+  void *ws = nullptr;
+  const df_status st = scratch_address(&ws);
+  if (st != DF_OK) return st;
+  return encode_device(kind, d_src, n, lengths, layout, d_bitstream, d_gaps, d_tile_out, d_sign_mantissa, ws,
+                       d_max_tile, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+df_status encode_device(df_kind kind, const void *d_src, uint64_t n, const uint8_t lengths[256],
+                        const df_info *layout, uint8_t *d_bitstream, uint8_t *d_gaps, uint64_t *d_tile_out,
+                        uint8_t *d_sign_mantissa, void *d_workspace, uint32_t *d_max_tile, hipStream_t stream) {
   if (!lengths || !layout || (kind != DF_KIND_BF16 && kind != DF_KIND_U8 && kind != DF_KIND_U4) ||
       layout->kind != kind || layout->n != n || !d_tile_out || !d_max_tile)
     return DF_ERR_ARG;
@@ -464,4 +526,4 @@ df_status df_encode_device(df_kind kind, const void *d_src, uint64_t n, const ui
   return hipGetLastError() == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace

@@ -70,6 +70,9 @@ _SIGNATURES = {
     "df_encode_device": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "df_encode_device_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "df_histogram": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
     "df_build_codebook": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "df_encode": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
@@ -408,6 +411,21 @@ def df_encode_device(kind: int, src: torch.Tensor, n: int, lengths, layout: df_i
                                   ctypes.byref(layout), ptr("bitstream"), ptr("gaps"), ptr("tile_out"), sm,
                                   ctypes.c_void_p(workspace.data_ptr()), ctypes.c_void_p(max_tile.data_ptr()),
                                   _stream_handle(stream, src.device)), "df_encode_device")
+
+
+ENCODE_SCRATCH_BYTES = 16 << 20   # df_encode_device_noalloc's workspace (DF_ENCODE_SCRATCH_BYTES)
+
+
+def df_encode_device_noalloc(kind: int, src: torch.Tensor, n: int, lengths, layout: df_info, sections: dict,
+                             max_tile: torch.Tensor, stream=None):
+    """df_encode_device with the library's static workspace (no allocation)."""
+    ln = np.ascontiguousarray(lengths, np.uint8)
+    ptr = lambda name: ctypes.c_void_p(sections[name].data_ptr())  # noqa: E731
+    sm = ptr("sign_mantissa") if kind == KIND_BF16 else None
+    _check(lib().df_encode_device_noalloc(kind, ctypes.c_void_p(src.data_ptr()), int(n), ln.ctypes.data,
+                                          ctypes.byref(layout), ptr("bitstream"), ptr("gaps"), ptr("tile_out"), sm,
+                                          ctypes.c_void_p(max_tile.data_ptr()), _stream_handle(stream, src.device)),
+           "df_encode_device_noalloc")
 
 
 def compress_device(kind: int, src: torch.Tensor, max_len: int = MAX_LEN, n=None, stream=None) -> DeviceContainer:
