@@ -213,8 +213,11 @@ int used_symbols(const uint8_t *len) {
 // the distinct 8(d+1)-bit stream prefixes of codes longer than 8(d+1) bits,
 // numbered after all shallower tables in order of (parent table, entry).
 // Leaves of length l in a depth-d table fill every entry whose low l - 8d
-// bits match the code's bits [8d, l).  Returns the table count or -1.
+// bits match the code's bits [8d, l).  Returns the table count or -1 (also
+// for lengths above 32 or beyond Kraft's inequality, as a damaged file may
+// hold: the tables are built before the container is validated).
 int build_tables(const uint8_t *len, std::vector<uint16_t> &lut) {
+  if (kraft_scaled(len) > (1ull << 32)) return -1;
   uint32_t code[256], rev[256];
   canonical_codes(len, code);
   for (int s = 0; s < 256; s++) rev[s] = len[s] ? stream_bits(code[s], len[s]) : 0;
@@ -703,6 +706,17 @@ df_status df_container_load(const char *path, df_container **out) {
   *out = nullptr;
   FILE *f = fopen(path, "rb");
   if (!f) return DF_ERR_IO;
+  // the file's size bounds every section size it may claim (a damaged size
+  // field must not turn into a huge allocation)
+  uint64_t file_bytes = 0;
+  if (fseek(f, 0, SEEK_END) == 0) {
+    const long e = ftell(f);
+    file_bytes = e > 0 ? (uint64_t)e : 0;
+  }
+  if (fseek(f, 0, SEEK_SET) != 0) {
+    fclose(f);
+    return DF_ERR_IO;
+  }
   FileHeader h;
   df_container *c = new (std::nothrow) df_container();
   df_status st = DF_OK;
@@ -725,7 +739,8 @@ df_status df_container_load(const char *path, df_container **out) {
     for (int s = 0; st == DF_OK && s < kStored; s++) {
       uint64_t b;
       uint8_t skip[56];
-      if (fread(&b, 8, 1, f) != 1 || fread(skip, 56, 1, f) != 1 || b > (1ull << 40)) {
+      const long at = ftell(f);
+      if (fread(&b, 8, 1, f) != 1 || fread(skip, 56, 1, f) != 1 || at < 0 || b > file_bytes - (uint64_t)at) {
         st = DF_ERR_FORMAT;
         break;
       }

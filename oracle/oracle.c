@@ -412,7 +412,7 @@ int oracle_encode(int kind, const void *src, uint64_t n, const uint8_t *lengths,
   if (oracle_canonical_codes(lengths, codes) != 0) return -1;
   memset(bitstream, 0, lay->bitstream_bytes);
   memset(gaps, 0, lay->gaps_bytes);
-  if (kind == O_KIND_BF16) memset(sm, 0, lay->sm_bytes);
+  if (kind == O_KIND_BF16 && lay->sm_bytes) memset(sm, 0, lay->sm_bytes);
   /* starts of every code, by definition: S_i = sum of earlier lengths */
   uint64_t pos = 0;
   uint64_t *first_start = (uint64_t *)malloc(sizeof(uint64_t) *
