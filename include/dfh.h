@@ -193,12 +193,19 @@ const char *df_status_string(df_status s);
 
 /* Borrowed device pointers to a container's sections (caller-owned, e.g.
  * torch tensors) plus its header scalars.  sign_mantissa is NULL unless the
- * kind is DF_KIND_BF16.  Every section must have the size df_info reports. */
+ * kind is DF_KIND_BF16.  Every section must have the size df_info reports.
+ * max_workgroups: 0 lets a launch take every workgroup slot the device has
+ * (the fastest decode on an otherwise idle GPU); a positive value caps the
+ * launch's workgroups (of up to 1024 lanes; at most two share a CU), so a
+ * decode on a side stream leaves most CUs to the kernels running beside it
+ * (the digest's "Descompressao por bloco de transformer": the next block is
+ * decompressed while the current one computes).  A batched launch takes the
+ * smallest positive cap of its views. */
 typedef struct {
   df_kind kind;
   uint32_t n_luts;
   uint32_t max_tile_elems;
-  uint32_t reserved;
+  uint32_t max_workgroups;
   uint64_t n;
   uint64_t total_bits;
   uint64_t n_threads;

@@ -218,7 +218,7 @@ struct Batch {
   uint32_t count;
   uint32_t lut_bytes;  // LDS reserved for hierarchical tables
   uint32_t out_bytes;  // LDS staging bytes per tile group
-  uint32_t pad;
+  uint32_t raise_prio;  // decode loops at a raised wave priority (not for capped launches)
   uint32_t *err;       // error word (checked launches only)
 };
 
@@ -882,8 +882,10 @@ void decode_kernel(const Batch batch) {
     // The decode loops (dependent lookup chains) run at a raised wave
     // priority, the store pass and the scan at the lowest: when waves of a
     // SIMD compete for issue, the chains go first and the stores fill in
-    // (measured: about 1% on the BF16 block, 3% on uint8).
-    __builtin_amdgcn_s_setprio(3);
+    // (measured: about 1% on the BF16 block, 3% on uint8).  A capped launch,
+    // which shares the CUs with kernels running beside it, stays at the base
+    // priority so that it does not take issue slots ahead of them.
+    if (batch.raise_prio) __builtin_amdgcn_s_setprio(3);
     // phase 1: count the codes that start in the lane's chunks
     int32_t rem_end = 0;  // E minus where the first chunk's walk stopped (<= 0)
     uint32_t kept_lo[kKeepRegs<KIND>], kept_hi[(kKeepRegs<KIND> + 1) / 2];
@@ -901,7 +903,7 @@ void decode_kernel(const Batch batch) {
                                         batch.err);
     }
 
-    __builtin_amdgcn_s_setprio(0);
+    if (batch.raise_prio) __builtin_amdgcn_s_setprio(0);
     // store the previous tile.  Its sign|mantissa registers are taken here,
     // once and on every path: the wait leaves the next step's stream words
     // in flight, and the store pass starts with no other load outstanding.
@@ -972,7 +974,7 @@ void decode_kernel(const Batch batch) {
       prev_dirty = d < out_bytes ? d : out_bytes;
     }
 
-    __builtin_amdgcn_s_setprio(3);
+    if (batch.raise_prio) __builtin_amdgcn_s_setprio(3);
     // phase 2: walk the same entries again (those phase 1 kept are replayed
     // from registers, the rest decoded again) and OR their symbol bytes into
     // the staging buffer until the lane's cnt codes are written.  The entry
@@ -1179,6 +1181,12 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     }
     if (groups == 0) return DF_ERR_ARG;
     uint64_t budget = (uint64_t)props.cus * (uint64_t)per_cu;
+    bool capped = false;
+    for (uint32_t k = 0; k < nj; k++) {  // the caller's cap, if any
+      const uint32_t cap = views[idx[k]].max_workgroups;
+      if (cap) capped = true;
+      if (cap && cap < budget) budget = cap;
+    }
     if (budget < nj) budget = nj;
     uint32_t wg = 0;
     for (uint32_t k = 0; k < nj; k++) {
@@ -1212,6 +1220,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     b.count = nj;
     b.lut_bytes = lut_bytes;
     b.out_bytes = out_bytes;
+    b.raise_prio = capped ? 0u : 1u;
     b.err = err;
     hipLaunchKernelGGL(fn, dim3(wg), dim3(groups * kTPB), lds, stream, b);
     if (hipGetLastError() != hipSuccess) return DF_ERR_HIP;

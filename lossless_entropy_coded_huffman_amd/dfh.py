@@ -45,7 +45,7 @@ class df_info(ctypes.Structure):
 
 class df_device_view(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("n_luts", ctypes.c_uint32),
-                ("max_tile_elems", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("max_tile_elems", ctypes.c_uint32), ("max_workgroups", ctypes.c_uint32),
                 ("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64),
                 ("n_threads", ctypes.c_uint64), ("n_tiles", ctypes.c_uint64),
                 ("bitstream", ctypes.c_void_p), ("gaps", ctypes.c_void_p),
@@ -537,28 +537,39 @@ def _check_dst(dc: DeviceContainer, dst: torch.Tensor):
         raise ValueError("dst must be a contiguous device tensor of at least %d bytes" % need)
 
 
-def df_decompress(dc: DeviceContainer, dst: torch.Tensor, stream=None):
+def _view(dc: DeviceContainer, max_workgroups) -> df_device_view:
+    """The container's view, with a workgroup cap when one is given."""
+    if not max_workgroups:
+        return dc.view
+    v = df_device_view.from_buffer_copy(dc.view)
+    v.max_workgroups = int(max_workgroups)
+    return v
+
+
+def df_decompress(dc: DeviceContainer, dst: torch.Tensor, stream=None, max_workgroups=None):
+    """max_workgroups: cap on the launch's workgroups (None or 0: no cap)."""
     _check_dst(dc, dst)
-    _check(lib().df_decompress(ctypes.byref(dc.view), ctypes.c_void_p(dst.data_ptr()),
+    _check(lib().df_decompress(ctypes.byref(_view(dc, max_workgroups)), ctypes.c_void_p(dst.data_ptr()),
                                _stream_handle(stream, dst.device)), "df_decompress")
 
 
-def df_decompress_checked(dc: DeviceContainer, dst: torch.Tensor, err: torch.Tensor, stream=None):
+def df_decompress_checked(dc: DeviceContainer, dst: torch.Tensor, err: torch.Tensor, stream=None,
+                          max_workgroups=None):
     """err: a device int32/uint32 tensor of one element, zeroed by the caller."""
     _check_dst(dc, dst)
     if not err.is_cuda or err.element_size() != 4:
         raise ValueError("err must be a 4-byte device tensor")
-    _check(lib().df_decompress_checked(ctypes.byref(dc.view), ctypes.c_void_p(dst.data_ptr()),
+    _check(lib().df_decompress_checked(ctypes.byref(_view(dc, max_workgroups)), ctypes.c_void_p(dst.data_ptr()),
                                        ctypes.c_void_p(err.data_ptr()),
                                        _stream_handle(stream, dst.device)), "df_decompress_checked")
 
 
-def df_decompress_batch(dcs, dsts, stream=None):
+def df_decompress_batch(dcs, dsts, stream=None, max_workgroups=None):
     if len(dcs) != len(dsts):
         raise ValueError("one destination per container")
     for dc, d in zip(dcs, dsts):
         _check_dst(dc, d)
-    views = (df_device_view * max(len(dcs), 1))(*[dc.view for dc in dcs])
+    views = (df_device_view * max(len(dcs), 1))(*[_view(dc, max_workgroups) for dc in dcs])
     ptrs = (ctypes.c_void_p * max(len(dsts), 1))(*[d.data_ptr() for d in dsts])
     dev = dsts[0].device if dsts else None
     _check(lib().df_decompress_batch(views, ptrs, len(dcs), _stream_handle(stream, dev)),

@@ -104,10 +104,14 @@ class CompressedBlocks:
 
     containers: one host container per block (BF16 kind, matrices in
     BlockShape.matrices() order).  Two scratch buffers of one block each are
-    allocated up front; the side stream has the default priority."""
+    allocated up front; the side stream has the default priority.
+    decode_workgroups caps the workgroups of a decode on the side stream
+    (0: no cap), so that it runs beside the block's kernels on the CUs they
+    leave rather than taking every CU."""
 
-    def __init__(self, containers, shape: BlockShape, device):
+    def __init__(self, containers, shape: BlockShape, device, decode_workgroups: int = 0):
         self.shape = shape
+        self.decode_workgroups = int(decode_workgroups)
         self.device = torch.device(device)
         n = shape.elements()
         for c in containers:
@@ -122,7 +126,7 @@ class CompressedBlocks:
     def _decode(self, i: int, main: torch.cuda.Stream):
         j = i % 2
         self.side.wait_event(self.released[j])
-        dfh.df_decompress(self.blocks[i], self.scratch[j], self.side)
+        dfh.df_decompress(self.blocks[i], self.scratch[j], self.side, max_workgroups=self.decode_workgroups)
         self.decoded[j].record(self.side)
 
     def forward(self, x: torch.Tensor, overlap: bool = True) -> torch.Tensor:

@@ -19,9 +19,9 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
-def run(torch, dev, shape, n_blocks, tokens, seed):
+def run(torch, dev, shape, n_blocks, tokens, seed, cap=0):
     host = fw.random_blocks(n_blocks, shape, seed)
-    model = fw.CompressedBlocks([dfh.compress(0, h) for h in host], shape, dev)
+    model = fw.CompressedBlocks([dfh.compress(0, h) for h in host], shape, dev, decode_workgroups=cap)
     g = torch.Generator(device="cpu").manual_seed(seed)
     x = (torch.randn(tokens, shape.hidden, generator=g) * 0.5).to(torch.bfloat16).to(dev)
     ref = fw.resident_forward(x, [fw.to_torch(h, dev) for h in host], shape)
@@ -43,3 +43,9 @@ def test_small_blocks_bit_identical(torch_dev):
 def test_llama3_8b_blocks_bit_identical(torch_dev):
     torch, dev = torch_dev
     run(torch, dev, fw.LLAMA3_8B, n_blocks=3, tokens=128, seed=0)
+
+
+def test_llama3_8b_blocks_capped_side_decode(torch_dev):
+    # the side-stream decode limited to 32 workgroups runs beside the blocks
+    torch, dev = torch_dev
+    run(torch, dev, fw.LLAMA3_8B, n_blocks=3, tokens=256, seed=1, cap=32)

@@ -260,3 +260,22 @@ def test_graph_instances_next_to_eager_launches(torch_dev, block):
         for e in execs:
             hg.L.hipGraphExecDestroy(e)
         hg.L.hipGraphDestroy(g)
+
+
+@pytest.mark.parametrize("cap", [1, 2, 7, 8, 33, 64, 300])
+def test_workgroup_cap(torch_dev, block, cap):
+    # a capped launch: few workgroups walk many steps (dynamically dealt
+    # units from step 3 on; one counter below eight workgroups)
+    torch, dev = torch_dev
+    dc, ref = block
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for checked in (False, True):
+        out.view(torch.int16).fill_(0)
+        if checked:
+            dfh.df_decompress_checked(dc, out, err, max_workgroups=cap)
+        else:
+            dfh.df_decompress(dc, out, max_workgroups=cap)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(out.view(torch.int16), ref), (cap, checked)
