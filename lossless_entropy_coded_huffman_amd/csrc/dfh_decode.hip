@@ -1050,6 +1050,7 @@ void decode_kernel(const Batch batch) {
 // ------------------------------------------------------------------ host side
 struct DeviceProps {
   bool ready;
+  int dev;
   int cus;
   int max_lds;
 };
@@ -1070,6 +1071,7 @@ df_status device_props(DeviceProps *out) {
   std::lock_guard<std::mutex> lk(g_mu);
   DeviceProps &p = g_props[dev];
   if (!p.ready) {
+    p.dev = dev;
     if (hipDeviceGetAttribute(&p.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipDeviceGetAttribute(&p.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
       return DF_ERR_HIP;
@@ -1084,6 +1086,37 @@ df_status device_props(DeviceProps *out) {
     p.ready = true;
   }
   *out = p;
+  return DF_OK;
+}
+
+// Resident workgroups per CU for a kernel, block size and LDS size, asked of
+// the runtime once per device and kept (the query costs tens of microseconds
+// of host time, which a launch of a small container would otherwise pay).
+struct OccEntry {
+  int dev;
+  KernelFn fn;
+  int threads;
+  size_t lds;
+  int occ;
+};
+constexpr int kOccCache = 256;
+OccEntry g_occ[kOccCache];
+int g_occ_n = 0;
+
+df_status occupancy(int dev, KernelFn fn, int threads, size_t lds, int *occ) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (int i = 0; i < g_occ_n; i++)
+      if (g_occ[i].dev == dev && g_occ[i].fn == fn && g_occ[i].threads == threads && g_occ[i].lds == lds) {
+        *occ = g_occ[i].occ;
+        return DF_OK;
+      }
+  }
+  int o = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, (const void *)fn, threads, lds) != hipSuccess) return DF_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_occ_n < kOccCache) g_occ[g_occ_n++] = {dev, fn, threads, lds, o};
+  *occ = o;
   return DF_OK;
 }
 
@@ -1169,9 +1202,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
                           (size_t)g * out_bytes + 16 * g + 64;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)fn, (int)(g * kTPB), need) !=
-          hipSuccess)
-        return DF_ERR_HIP;
+      if (occupancy(props.dev, fn, (int)(g * kTPB), need, &occ) != DF_OK) return DF_ERR_HIP;
       if (occ < 1) continue;
       if (groups == 0 || (uint64_t)occ * g > (uint64_t)per_cu * groups) {
         groups = g;
