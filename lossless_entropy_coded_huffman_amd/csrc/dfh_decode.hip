@@ -218,7 +218,7 @@ struct Batch {
   uint32_t count;
   uint32_t lut_bytes;  // LDS reserved for hierarchical tables
   uint32_t out_bytes;  // LDS staging bytes per tile group
-  uint32_t raise_prio;  // decode loops at a raised wave priority (not for capped launches)
+  uint32_t pad;
   uint32_t *err;       // error word (checked launches only)
 };
 
@@ -673,7 +673,12 @@ __device__ __forceinline__ v4u clean_tab(v4u v, uint32_t word, uint32_t *err) {
   return v;
 }
 
-template <int KIND, bool CHECKED>
+// PRIO: the decode loops run at a raised wave priority (the default); a
+// launch with a workgroup cap, which shares the CUs with kernels running
+// beside it, uses PRIO = false and stays at the base priority.  (A runtime
+// flag instead of a template parameter cost the BF16 kernel registers and
+// 1.2% of its time.)
+template <int KIND, bool CHECKED, bool PRIO>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
   // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
@@ -882,10 +887,11 @@ void decode_kernel(const Batch batch) {
     // The decode loops (dependent lookup chains) run at a raised wave
     // priority, the store pass and the scan at the lowest: when waves of a
     // SIMD compete for issue, the chains go first and the stores fill in
-    // (measured: about 1% on the BF16 block, 3% on uint8).  A capped launch,
-    // which shares the CUs with kernels running beside it, stays at the base
-    // priority so that it does not take issue slots ahead of them.
-    if (batch.raise_prio) __builtin_amdgcn_s_setprio(3);
+    // (measured: about 1% on the BF16 block, 3% on uint8).  A capped launch
+    // (PRIO = false), which shares the CUs with kernels running beside it,
+    // stays at the base priority so that it does not take issue slots ahead
+    // of them.
+    if (PRIO) __builtin_amdgcn_s_setprio(3);
     // phase 1: count the codes that start in the lane's chunks
     int32_t rem_end = 0;  // E minus where the first chunk's walk stopped (<= 0)
     uint32_t kept_lo[kKeepRegs<KIND>], kept_hi[(kKeepRegs<KIND> + 1) / 2];
@@ -903,7 +909,7 @@ void decode_kernel(const Batch batch) {
                                         batch.err);
     }
 
-    if (batch.raise_prio) __builtin_amdgcn_s_setprio(0);
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
     // store the previous tile.  Its sign|mantissa registers are taken here,
     // once and on every path: the wait leaves the next step's stream words
     // in flight, and the store pass starts with no other load outstanding.
@@ -974,7 +980,7 @@ void decode_kernel(const Batch batch) {
       prev_dirty = d < out_bytes ? d : out_bytes;
     }
 
-    if (batch.raise_prio) __builtin_amdgcn_s_setprio(3);
+    if (PRIO) __builtin_amdgcn_s_setprio(3);
     // phase 2: walk the same entries again (those phase 1 kept are replayed
     // from registers, the rest decoded again) and OR their symbol bytes into
     // the staging buffer until the lane's cnt codes are written.  The entry
@@ -1059,10 +1065,16 @@ DeviceProps g_props[kMaxDevices];
 std::mutex g_mu;
 
 typedef void (*KernelFn)(const Batch);
-KernelFn kernel_for(df_kind kind, bool checked) {
-  if (kind == DF_KIND_BF16) return checked ? decode_kernel<DF_KIND_BF16, true> : decode_kernel<DF_KIND_BF16, false>;
-  if (kind == DF_KIND_U4) return checked ? decode_kernel<DF_KIND_U4, true> : decode_kernel<DF_KIND_U4, false>;
-  return checked ? decode_kernel<DF_KIND_U8, true> : decode_kernel<DF_KIND_U8, false>;
+template <int KIND>
+KernelFn kernel_of(bool checked, bool prio) {
+  if (checked) return prio ? decode_kernel<KIND, true, true> : decode_kernel<KIND, true, false>;
+  return prio ? decode_kernel<KIND, false, true> : decode_kernel<KIND, false, false>;
+}
+
+KernelFn kernel_for(df_kind kind, bool checked, bool prio) {
+  if (kind == DF_KIND_BF16) return kernel_of<DF_KIND_BF16>(checked, prio);
+  if (kind == DF_KIND_U4) return kernel_of<DF_KIND_U4>(checked, prio);
+  return kernel_of<DF_KIND_U8>(checked, prio);
 }
 
 df_status device_props(DeviceProps *out) {
@@ -1079,8 +1091,8 @@ df_status device_props(DeviceProps *out) {
     // opt-in the call may fail, which is harmless, so its error is cleared
     const df_kind kinds[3] = {DF_KIND_BF16, DF_KIND_U8, DF_KIND_U4};
     for (df_kind k : kinds)
-      for (int c = 0; c < 2; c++)
-        if (hipFuncSetAttribute((const void *)kernel_for(k, c != 0),
+      for (int c = 0; c < 4; c++)
+        if (hipFuncSetAttribute((const void *)kernel_for(k, (c & 1) != 0, (c & 2) != 0),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.max_lds - 64) != hipSuccess)
           (void)hipGetLastError();
     p.ready = true;
@@ -1169,7 +1181,11 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
   DeviceProps props;
   df_status st = device_props(&props);
   if (st != DF_OK) return st;
-  KernelFn fn = kernel_for(kind, checked);
+  // a capped launch (any view with a workgroup cap) keeps its waves at the
+  // base priority
+  bool capped = false;
+  for (uint32_t i = 0; i < count; i++) capped = capped || views[i].max_workgroups != 0;
+  KernelFn fn = kernel_for(kind, checked, !capped);
 
   for (uint32_t base = 0; base < count; base += DF_MAX_BATCH) {
     const uint32_t m = count - base < DF_MAX_BATCH ? count - base : DF_MAX_BATCH;
@@ -1212,10 +1228,8 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     }
     if (groups == 0) return DF_ERR_ARG;
     uint64_t budget = (uint64_t)props.cus * (uint64_t)per_cu;
-    bool capped = false;
     for (uint32_t k = 0; k < nj; k++) {  // the caller's cap, if any
       const uint32_t cap = views[idx[k]].max_workgroups;
-      if (cap) capped = true;
       if (cap && cap < budget) budget = cap;
     }
     if (budget < nj) budget = nj;
@@ -1251,7 +1265,6 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     b.count = nj;
     b.lut_bytes = lut_bytes;
     b.out_bytes = out_bytes;
-    b.raise_prio = capped ? 0u : 1u;
     b.err = err;
     hipLaunchKernelGGL(fn, dim3(wg), dim3(groups * kTPB), lds, stream, b);
     if (hipGetLastError() != hipSuccess) return DF_ERR_HIP;

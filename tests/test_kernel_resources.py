@@ -33,8 +33,9 @@ def kernels(tmp_path_factory):
     return meta
 
 
-def test_six_decode_kernels(kernels):
-    assert len(kernels) == 6   # three kinds, checked and unchecked
+def test_twelve_decode_kernels(kernels):
+    # three kinds, checked and unchecked, at raised and base wave priority
+    assert len(kernels) == 12
 
 
 def test_no_scratch_and_64_vgprs(kernels):
