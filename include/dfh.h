@@ -67,10 +67,11 @@
  *                  of codes; 0 = first code longer than 12 bits.
  *                  uint8: uint32[8192] indexed by 13 bits, up to two codes
  *                  (6.6-bit codes rarely leave room for a third): bits 0..3
- *                  bits consumed, 8..15 symbol of code 0, 16..23 symbol of
- *                  code 1 (0 when one code), 24..31 number of codes; 0 =
- *                  first code longer than 13 bits.  Then uint8[256]: the
- *                  code length of each symbol.  DF_DTAB_BYTES_U8 bytes.
+ *                  bits consumed, 4..7 zero, 8..15 symbol of code 0,
+ *                  16..23 symbol of code 1 (0 when one code), 24..31
+ *                  number of codes; 0 = first code longer than 13 bits.
+ *                  Then uint8[256]: the code length of each symbol.
+ *                  DF_DTAB_BYTES_U8 bytes.
  * n_threads = floor(start of last code / 64) + 1 (0 when n == 0) and
  * n_tiles = ceil(n_threads / 256).
  */
