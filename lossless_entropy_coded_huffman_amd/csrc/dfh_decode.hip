@@ -29,10 +29,13 @@
 //     gap field): at 6.6-bit codes a chunk holds ten codes, and the step's
 //     fixed cost (loads, offsets, scan, barriers) is then spread over
 //     twenty;
-//   - a group stores a tile one step late: the store pass of tile k shares a
-//     barrier interval with the count of tile k + 1, so HBM traffic overlaps
-//     the decode; the sign|mantissa bytes it merges are requested at the top
-//     of the step, before the count;
+//   - a BF16 or uint4 group stores a tile one step late: the store pass of
+//     tile k shares a barrier interval with the count of tile k + 1, so HBM
+//     traffic overlaps the decode; the sign|mantissa bytes it merges are
+//     requested at the top of the step, before the count.  A uint8 wave
+//     stores its own lanes' output range as soon as its phase 2 is done
+//     (plain byte staging needs no clearing, so no group barrier ends the
+//     step);
 //   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes;
 //     uint8: its 16 bytes plus the next 4) in registers and walks each chunk
 //     as a 96-bit window shifted with funnel shifts;
@@ -48,7 +51,8 @@
 //     them, merges the sign|mantissa bytes (BF16), packs nibbles (uint4) and
 //     issues 16-byte global stores, one in flight per lane (BF16),
 //     non-temporal for BF16 and uint4; BF16 also reads its streams
-//     non-temporally;
+//     non-temporally; the bytes of a uint8 range's partial first and last
+//     granules are stored one per lane;
 //   - the decode loops run at a raised wave priority, the store pass at the
 //     lowest; the uint4 and uint8 kernels replay phase 1's first table
 //     entries from registers in phase 2.
@@ -395,7 +399,8 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
   }
 }
 
-// The store pass of one tile: aligned 16-byte stores of output elements
+// The store pass of one tile (BF16 and uint4; uint8 waves store their own
+// ranges in the step loop): aligned 16-byte stores of output elements
 // [a + lo_r, a + hi_r) from the staging buffer at LDS byte buf; BF16 merges
 // each granule's exponents with its sign|mantissa bytes (the first
 // kPrefetch granules of each lane arrive in smv, the rest are loaded here).
@@ -406,8 +411,8 @@ __device__ __forceinline__ void store_partial(uint8_t *dst, uint32_t e0, uint32_
 // stream and sign|mantissa loads that the decode waits on, and the kernel
 // ran about 5% slower.
 //
-// The pass also leaves the staging buffer zero for the next tile's ORs
-// (BF16 and uint4; uint8 stores plain bytes): each lane clears the granules
+// The pass also leaves the staging buffer zero for the next tile's ORs:
+// each lane clears the granules
 // it has just read, and the bytes from the last granule up to `dirty` (the
 // next lane-group's lookahead slack) are cleared here too.
 //
@@ -419,10 +424,10 @@ template <int KIND>
 __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t a, uint32_t lo_r,
                                            uint32_t hi_r, uint32_t he, uint32_t ngroups, uint32_t dirty,
                                            const uint2 (&smv)[kPrefetch], uint32_t lane) {
-  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : KIND == DF_KIND_U8 ? 16u : 32u;
-  if (KIND != DF_KIND_U8)  // (uint8 staging is stored plainly, never ORed)
-    for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
-      *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
+  static_assert(KIND != DF_KIND_U8, "uint8 waves store their own ranges");
+  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : 32u;
+  for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
+    *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
   if (KIND == DF_KIND_BF16) {
     uint16_t *dst_t = (uint16_t *)jb.dst + a;
     const uint8_t *sm_t = jb.sm + a;
@@ -479,15 +484,6 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
       // non-temporal: 2.4% faster on the uint4 block (uint8 the same)
       if (b0 >= blo && b0 + 16 <= bhi) __builtin_nontemporal_store((v4u){o.x, o.y, o.z, o.w}, (v4u *)(dst_t + b0));
       else store_partial(dst_t, b0, blo, bhi, o);
-    }
-  } else {
-    uint8_t *dst_t = (uint8_t *)jb.dst + a;
-    lds_v4 *ex_t = lds<lds_v4>(buf);
-    for (uint32_t g = lane; g < ngroups; g += kTPB) {
-      const uint32_t e0 = 16 * g;
-      const v4u v = ex_t[g];
-      if (e0 >= lo_r && e0 + 16 <= hi_r) *(v4u *)(dst_t + e0) = v;
-      else store_partial(dst_t, e0, lo_r, hi_r, make_uint4(v.x, v.y, v.z, v.w));
     }
   }
 }
@@ -785,7 +781,7 @@ void decode_kernel(const Batch batch) {
   // unit stride, 6 the counter's last value, 7 the counter c, plus 16 once
   // its last value has been taken, plus 32 when the workgroup deals units to
   // itself, 8..9 the key, 10 the number of counters
-  lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 16 * groups);
+  lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 32 * groups);
   if (dyn && tid == 0) {
     const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
     const uint32_t parts = nwg / 8 < kParts ? (nwg / 8 ? nwg / 8 : 1u) : kParts;
@@ -843,6 +839,7 @@ void decode_kernel(const Batch batch) {
   uint64_t prev_a = 0;
   uint32_t prev_lo = 0, prev_hi = 0, prev_he = 0, prev_ng = 0, prev_dirty = 0;
 
+  uint32_t par = 0;  // step parity
   for (; base < n_spans;) {
     const uint32_t tile = base + grp;  // the span, wave-uniform
     const bool active = tile < n_spans;
@@ -935,9 +932,11 @@ void decode_kernel(const Batch batch) {
     // in flight, and the store pass starts with no other load outstanding.
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    if (have_prev)
-      store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
-    have_prev = active;
+    if constexpr (KIND != DF_KIND_U8) {
+      if (have_prev)
+        store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
+    }
+    have_prev = KIND != DF_KIND_U8 && active;
     prev_a = a;
     prev_lo = lo_r;
     prev_hi = hi_r;
@@ -947,7 +946,11 @@ void decode_kernel(const Batch batch) {
     // prefix sum of the counts over the tile's 256 lanes
     const uint32_t wid = tid >> 6;
     const uint32_t x = wave_inclusive_sum(cnt);
-    if ((tid & 63) == 63) wsum[wid] = x;
+    // (uint8: two sets of sums, by step parity: its steps end without a
+    // barrier, so a wave may write next step's sums while another still
+    // reads these)
+    const uint32_t wset = KIND == DF_KIND_U8 ? 4 * groups * par : 0u;
+    if ((tid & 63) == 63) wsum[wset + wid] = x;
     if (dyn && tid == 0) {  // last step's grab, for the workgroup: its first tile
       uint32_t pub = 0xFFFFFFFFu;  // no tile: past any span index
       if (grabbed) {
@@ -987,7 +990,7 @@ void decode_kernel(const Batch batch) {
         tk = ctr ? __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : tk + 1;
       }
     }
-    const lds_u32 *ws = wsum + 4 * grp;
+    const lds_u32 *ws = wsum + wset + 4 * grp;
     const uint32_t s0 = ws[0], s1 = ws[1], s2 = ws[2], s3 = ws[3];
     // the wave's index in its group; read as a uniform value in the BF16
     // kernel, whose compares on it were lane masks kept across the loop
@@ -1047,7 +1050,46 @@ void decode_kernel(const Batch batch) {
                               __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
-    __syncthreads();
+    if constexpr (KIND == DF_KIND_U8) {
+      // uint8: each wave stores its own output range as soon as its phase 2
+      // is done.  Its lanes' codes are output elements [r0, r1) of the span,
+      // staged by this wave (a neighbour's lookahead writes bytes of the
+      // range with the same values), so the store needs no barrier; the
+      // next step's phase 2 writes staging only after the scan barrier,
+      // which every wave reaches after its store, and the sums are read
+      // from the other set next step.  Against the group's store pass one
+      // step late (with its end-of-step barrier), and with the range's
+      // partial first and last granules stored one byte per lane rather
+      // than byte by byte in one lane, the uint8 block went from 195 to
+      // 171 us side by side.  The store runs at the base priority (at the
+      // decode's it was 5% slower).
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
+      if (active) {
+        const uint32_t tot = hi_r - lo_r;
+        uint32_t w0 = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u);
+        uint32_t w1 = w0 + (wq == 0 ? s0 : wq == 1 ? s1 : wq == 2 ? s2 : s3);
+        // (damaged counts: each bound limited to the span first)
+        w0 = w0 < tot ? w0 : tot;
+        w1 = w1 < tot ? (w1 < w0 ? w0 : w1) : tot;
+        const uint32_t r0 = lo_r + w0, r1 = lo_r + w1;
+        uint8_t *dst_t = (uint8_t *)jb.dst + a;
+        const lds_v4 *ex_t = lds<const lds_v4>(buf);
+        const uint32_t l = lane & 63;
+        // the granules wholly inside [r0, r1): one 16-byte store each
+        const uint32_t fs = (r0 + 15) / 16, fe = r1 / 16;
+        for (uint32_t g = fs + l; g < fe; g += 64) *(v4u *)(dst_t + 16 * g) = ex_t[g];
+        // the bytes of the first and last granule that are not whole: one
+        // byte per lane, lanes 0..15 the first granule, 16..31 the last
+        if (l < 32 && r0 < r1) {
+          const uint32_t p = 16 * (l < 16 ? r0 / 16 : (r1 - 1) / 16) + (l & 15);
+          if (p >= r0 && p < r1 && (p < 16 * fs || p >= 16 * fe)) dst_t[p] = *lds<const lds_u8>(buf + p);
+        }
+      }
+    } else {
+      __syncthreads();
+    }
+    par ^= 1u;
     if constexpr (kDynamic<KIND>) {
       base = base_nxt;
       base_nxt = base_nxt2;
@@ -1058,18 +1100,20 @@ void decode_kernel(const Batch batch) {
   // a workgroup that took its counter's last value counts it finished (the
   // last counter of the slot to finish frees the slot)
   if (dyn && tid == 0 && (nx_lds[7] & 16) && nx_lds[1] != kNoTicket) counter_finished(nx_lds[1], nx_lds[10]);
-  // the last tile of this group
-  if (have_prev) {
-    uint2 smv[kPrefetch];
+  // the last tile of this group (BF16 and uint4)
+  if constexpr (KIND != DF_KIND_U8) {
+    if (have_prev) {
+      uint2 smv[kPrefetch];
 #pragma unroll
-    for (uint32_t k = 0; k < kPrefetch; k++) {
-      const uint32_t g = lane + k * kTPB;
-      smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * (uint64_t)g)
-                                                    : make_uint2(0, 0);
+      for (uint32_t k = 0; k < kPrefetch; k++) {
+        const uint32_t g = lane + k * kTPB;
+        smv[k] = KIND == DF_KIND_BF16 && g < prev_ng ? *(const uint2 *)(jb.sm + prev_a + 8 * (uint64_t)g)
+                                                      : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
+      store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
     }
-#pragma unroll
-    for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
   }
 }
 
@@ -1235,7 +1279,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
       const size_t need = (size_t)(kind == DF_KIND_U8 ? kTabBytes<DF_KIND_U8> : kDtabBytes) + lut_bytes +
-                          (size_t)g * out_bytes + 16 * g + 64;
+                          (size_t)g * out_bytes + 32 * g + 64;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (occupancy(props.dev, fn, (int)(g * kTPB), need, &occ) != DF_OK) return DF_ERR_HIP;
