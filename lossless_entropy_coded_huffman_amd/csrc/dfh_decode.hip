@@ -337,11 +337,6 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
   __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// In place of a table entry whose first code is longer than the index width:
-// an entry for that one code (symbol byte in the low word for phase 2).  A
-// 32-bit code, whose length does not fit the five-bit field, drops one
-// stream word here and reports 0 bits (phase 1 takes the 32 bits off its
-// budget itself).
 // Stores a pair-table entry's symbol bytes (bits 8..23) at staging byte q:
 // the first always, the second when the entry holds two codes.  uint8 lanes
 // store plain bytes rather than OR words: every byte a lane stores is either
@@ -356,6 +351,11 @@ __device__ __forceinline__ void put_pair(uint32_t q, uint32_t h) {
   if (h >= 2u << 24) p[1] = (uint8_t)(h >> 16);
 }
 
+// In place of a table entry whose first code is longer than the index width:
+// an entry for that one code (symbol byte in the low word for phase 2).  A
+// 32-bit code, whose length does not fit the five-bit field, drops one
+// stream word here and reports 0 bits (phase 1 takes the 32 bits off its
+// budget itself).
 template <int KIND, bool CHECKED>
 __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *err) {
   const uint32_t c = long_code<KIND, CHECKED>(n_luts, t.b0, err);
@@ -386,7 +386,9 @@ __device__ __forceinline__ uint2 load_nt2(const void *p) {
 // elements over lanes, their sign|mantissa bytes read from the granule's
 // lane, made the BF16 block 29% slower; every wave then read the last
 // granule lane's prefetch register before its loop, so it waited for its
-// prefetched loads at once rather than one granule at a time.)
+// prefetched loads at once rather than one granule at a time.  Handing the
+// merged granule to eight lanes of the owner's wave through LDS instead
+// measured the same as these stores: BF16 is bound by its memory path.)
 __device__ __forceinline__ void store_partial(uint16_t *dst, uint32_t e0, uint32_t lo, uint32_t hi, uint4 o) {
 #pragma unroll
   for (uint32_t i = 0; i < 8; i++) {
