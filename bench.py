@@ -25,6 +25,7 @@ Other workloads (--workload) are for local measurement; the default is the
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import statistics
@@ -311,7 +312,12 @@ def main():
     # several microseconds each and would be timed as part of the decode.
     # The mean launch duration is that span over the launch count (so it
     # includes the dispatch gap between launches).
+    # Python's cyclic collector runs before the region and not inside it: a
+    # full collection can take tens of milliseconds, several times the whole
+    # region at --steps 20.
     region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record(stream)
@@ -321,6 +327,7 @@ def main():
     region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     mean_ms = region[0].elapsed_time(region[1]) / (args.steps * per_step)
     # spread of single launches, each between its own events, after the
     # timed region (these figures carry the event overhead)

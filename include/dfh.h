@@ -64,7 +64,9 @@
  *                  0..3 (BF16: exponent rotated right by one bit), 32..36
  *                  bits consumed, 37..47 flags for codes starting at window
  *                  bits 1..11, 48..55 symbol byte of code 4, 56..63 number
- *                  of codes; 0 = first code longer than 12 bits.
+ *                  of codes; 0 = first code longer than 12 bits.  uint4
+ *                  holds its symbols as nibbles instead: bits 0..19 the
+ *                  low nibbles of codes 0..4, bits 20..31 and 48..55 zero.
  *                  uint8: uint32[8192] indexed by 13 bits, up to two codes
  *                  (6.6-bit codes rarely leave room for a third): bits 0..3
  *                  bits consumed, 4..7 zero, 8..15 symbol of code 0,

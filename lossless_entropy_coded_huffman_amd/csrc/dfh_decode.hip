@@ -44,15 +44,15 @@
 //     the hierarchical tables;
 //   - the per-tile prefix sum is a wave64 DPP scan (row_shr, row_bcast) plus
 //     one LDS step across the group's four waves;
-//   - phase 2 ORs the decoded bytes into the group's LDS staging buffer
-//     (uint8: plain byte stores),
-//     whose byte j holds output element (tile start rounded down to the
-//     store granule) + j; the store pass reads aligned LDS words, clears
-//     them, merges the sign|mantissa bytes (BF16), packs nibbles (uint4) and
-//     issues 16-byte global stores, one in flight per lane (BF16),
-//     non-temporal for BF16 and uint4; BF16 also reads its streams
-//     non-temporally; the bytes of a uint8 range's partial first and last
-//     granules are stored one per lane;
+//   - phase 2 ORs the decoded symbols into the group's LDS staging buffer
+//     (uint8: plain byte stores), whose byte j holds output element (tile
+//     start rounded down to the store granule) + j, or for uint4 whose
+//     nibble j does (the output's own packing, two elements per byte); the
+//     store pass reads aligned LDS words, clears them, merges the
+//     sign|mantissa bytes (BF16) and issues 16-byte global stores, one in
+//     flight per lane (BF16), non-temporal for BF16 and uint4; BF16 also
+//     reads its streams non-temporally; the bytes of a partial first or last
+//     granule of a uint4 tile or a uint8 range are stored one per lane;
 //   - the decode loops run at a raised wave priority, the store pass at the
 //     lowest; the uint4 and uint8 kernels replay phase 1's first table
 //     entries from registers in phase 2.
@@ -83,9 +83,11 @@ constexpr uint32_t kPrefetch = 4;  // sign|mantissa 8-byte groups requested ahea
 // s_waitcnt operand (gfx9 encoding: vmcnt in bits 3..0 and 15..14, expcnt
 // in 6..4, lgkmcnt in 11..8) that waits for vmcnt 0 only
 constexpr int kWaitVm0 = 0x0F70;
-// staging bytes past a tile's last element that phase 2 may touch: up to four
-// lookahead symbol bytes, widened to the two words of one OR
-constexpr uint32_t kSlack = 12;
+// staging positions past a tile's last element that phase 2 may touch: BF16
+// and uint8 bytes, up to four lookahead symbol bytes widened to the two words
+// of one OR; uint4 nibbles, the two words of one OR (16 nibbles)
+template <int KIND>
+constexpr uint32_t kSlack = KIND == DF_KIND_U4 ? 16u : 12u;
 // Table entries phase 1 keeps in registers for phase 2 to replay; a lane
 // with more walks the rest of its chunk again from where the kept ones end.
 // Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
@@ -293,14 +295,6 @@ __device__ __forceinline__ uint2 merge4(uint32_t e4, uint32_t s4) {
   return make_uint2((x0 & 0x7F7F7F7Fu) | (y0 & 0x80808080u), (x1 & 0x7F7F7F7Fu) | (y1 & 0x80808080u));
 }
 
-// Eight uint4 symbols, one per byte in two words (elements 0..3, 4..7), as
-// four packed bytes, element 2j in the low nibble of byte j: t = w | w >> 4
-// puts pair (2j, 2j + 1) in byte 2j of each word, a byte permute gathers
-// bytes 0 and 2 of both.
-__device__ __forceinline__ uint32_t pack8(uint32_t w0, uint32_t w1) {
-  return __builtin_amdgcn_perm(w1 | (w1 >> 4), w0 | (w0 >> 4), 0x06040200u);
-}
-
 // A lane's position in its stream words: b2:b1:b0 holds the stream from
 // the current code on (bit 0 of b0 = first bit of the next code).  Built
 // from the chunk's three words w2:w1:w0 and the bit g (< 32) at which the
@@ -337,6 +331,19 @@ __device__ __forceinline__ void or_entry(uint32_t q, v2u e) {
   __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// uint4: ORs an entry's symbols (nibbles, low word bits 0..19) into the
+// staging buffer at nibble q (nibble 2j + i of the buffer is the low (i = 0)
+// or high nibble of byte j, the output's own packing).  Against byte staging
+// packed into nibbles by the store pass, the uint4 block went from 76.7 to
+// 71.0 us side by side: the store pass copies granules, and reads and
+// clears half the LDS bytes.
+__device__ __forceinline__ void or_nibbles(uint32_t q, uint32_t x) {
+  const uint64_t v = (uint64_t)x << ((q & 7) * 4);
+  lds_u32 *w = lds<lds_u32>((q >> 3) << 2);
+  __hip_atomic_fetch_or(w, (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_or(w + 1, (uint32_t)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Stores a pair-table entry's symbol bytes (bits 8..23) at staging byte q:
 // the first always, the second when the entry holds two codes.  uint8 lanes
 // store plain bytes rather than OR words: every byte a lane stores is either
@@ -366,7 +373,7 @@ __device__ __forceinline__ v2u long_entry(uint32_t n_luts, Stream &t, uint32_t *
     t.b2 = 0;
     len = 0;
   }
-  const uint32_t sym = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : (c & 0xFFu);
+  const uint32_t sym = KIND == DF_KIND_BF16 ? rot_right1(c & 0xFFu) : KIND == DF_KIND_U4 ? (c & 0xFu) : (c & 0xFFu);
   if (KIND == DF_KIND_U8) return (v2u){0u, kOneCode | (sym << 8) | len};  // a pair-table entry
   return (v2u){sym, kOneCode | len};
 }
@@ -423,7 +430,7 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
                                            uint32_t hi_r, uint32_t he, uint32_t ngroups, uint32_t dirty,
                                            const uint2 (&smv)[kPrefetch], uint32_t lane) {
   static_assert(KIND != DF_KIND_U8, "uint8 waves store their own ranges");
-  const uint32_t gbytes = KIND == DF_KIND_BF16 ? 8u : 32u;
+  const uint32_t gbytes = 16u / (KIND == DF_KIND_BF16 ? 2u : 1u);  // staging bytes per store granule
   for (uint32_t o = gbytes * ngroups + 8 * lane; o < dirty; o += 8 * kTPB)
     *lds<lds_v2>(buf + o) = (v2u){0u, 0u};
   if (KIND == DF_KIND_BF16) {
@@ -472,10 +479,8 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
     // to 77.2 us side by side)
     const uint32_t fs = (blo + 15) / 16, fe = bhi / 16;
     for (uint32_t g = fs + lane; g < fe; g += kTPB) {
-      const v4u x0 = ex_t[2 * g], x1 = ex_t[2 * g + 1];
-      ex_t[2 * g] = (v4u){0u, 0u, 0u, 0u};
-      ex_t[2 * g + 1] = (v4u){0u, 0u, 0u, 0u};
-      uint4 o = make_uint4(pack8(x0.x, x0.y), pack8(x0.z, x0.w), pack8(x1.x, x1.y), pack8(x1.z, x1.w));
+      v4u o = ex_t[g];
+      ex_t[g] = (v4u){0u, 0u, 0u, 0u};
       const uint32_t b0 = 16 * g;
       if (kill - b0 < 16) {
         const uint32_t m = ~(0xF0u << (8 * ((kill - b0) & 3)));
@@ -486,20 +491,19 @@ __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t
         o.w &= wk == 3 ? m : ~0u;
       }
       // non-temporal: 2.4% faster on the uint4 block (uint8 the same)
-      __builtin_nontemporal_store((v4u){o.x, o.y, o.z, o.w}, (v4u *)(dst_t + b0));
+      __builtin_nontemporal_store(o, (v4u *)(dst_t + b0));
     }
     // (granules 0 and ngroups - 1 are the only ones outside [fs, fe), as
     // blo <= 16 and 16 (ngroups - 1) < bhi; each is read and cleared whole,
-    // its 32 staging bytes, also where the tile owns none of its output
+    // its 16 staging bytes, also where the tile owns none of its output
     // bytes)
     if (lane < 32 && ngroups > 0) {
       const uint32_t g = lane < 16 ? 0u : ngroups - 1;
       const uint32_t p = 16 * g + (lane & 15);
       if (g < fs || g >= fe) {
-        lds_u16 *pair = lds<lds_u16>(buf + 2 * p);
-        const uint32_t v = *pair;
-        *pair = 0;
-        uint32_t byte = (v & 0x0Fu) | ((v >> 4) & 0xF0u);
+        lds_u8 *sb = lds<lds_u8>(buf + p);
+        uint32_t byte = *sb;
+        *sb = 0;
         if (p == kill) byte &= 0x0Fu;
         if (p >= blo && p < bhi) dst_t[p] = (uint8_t)byte;
       }
@@ -644,9 +648,9 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
       if (KIND == DF_KIND_U8) {
         put_pair(q, kept_lo[k]);
         q += kept_lo[k] >> 24;
-      } else {
+      } else {  // (uint4: BF16 keeps none)
         const uint32_t hi = (k & 1) ? kept_hi[k / 2] & 0xFFFF0000u : kept_hi[k / 2] << 16;
-        or_entry(q, (v2u){kept_lo[k], hi});
+        or_nibbles(q, kept_lo[k]);
         q += hi >> 24;
       }
     }
@@ -663,7 +667,8 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
       v2u e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
       if (e.y < kOneCode) e = long_entry<KIND, CHECKED>(n_luts, t, err);  // rare
       drop(t, e.y);
-      or_entry(q, e);
+      if (KIND == DF_KIND_U4) or_nibbles(q, e.x);
+      else or_entry(q, e);
       q += e.y >> 24;
     }
   }
@@ -1017,8 +1022,10 @@ void decode_kernel(const Batch batch) {
     const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
-    {  // bytes phase 2 may write: every lane ends by lo_r + off + cnt + 7
-      const uint32_t d = (lo_r + s0 + s1 + s2 + s3 + kSlack + 7) & ~7u;
+    {  // staging bytes phase 2 may write: every lane ends by lo_r + off + cnt
+       // + the slack (uint4: nibbles, two per byte)
+      const uint32_t e = lo_r + s0 + s1 + s2 + s3 + kSlack<KIND>;
+      const uint32_t d = ((KIND == DF_KIND_U4 ? (e + 1) / 2 : e) + 7) & ~7u;
       prev_dirty = d < out_bytes ? d : out_bytes;
     }
 
@@ -1034,11 +1041,13 @@ void decode_kernel(const Batch batch) {
     // whose codes would not fit the buffer (only with corrupt offsets or
     // stream) skips the phase, so LDS writes stay inside the buffer.
     {
-      uint32_t q = buf + lo_r + off;
+      // staging positions: bytes, uint4 nibbles (two per byte)
+      const uint32_t cap = KIND == DF_KIND_U4 ? 2 * out_bytes : out_bytes;
+      uint32_t q = (KIND == DF_KIND_U4 ? 2 * buf : buf) + lo_r + off;
       uint32_t qend = q + cnt;
       // (each term is bounded first, so the sum cannot wrap even when a
       // damaged table makes the counts meaningless)
-      const bool fits = off <= out_bytes && cnt <= out_bytes && lo_r + off + cnt + kSlack <= out_bytes;
+      const bool fits = off <= cap && cnt <= cap && lo_r + off + cnt + kSlack<KIND> <= cap;
       if (!fits) {
         qend = q;
         if (CHECKED) atomicOr(batch.err, DF_DEVERR_COUNT);
@@ -1065,7 +1074,7 @@ void decode_kernel(const Batch batch) {
                            : p >= 32 ? __builtin_amdgcn_alignbit(cur.w2, cur.w1, p - 32)
                                      : __builtin_amdgcn_alignbit(cur.w1, cur.w0, p);
         const uint32_t c = long_code<KIND, CHECKED>(n_luts, win, batch.err);
-        __hip_atomic_fetch_or(lds<lds_u32>(q & ~3u), (c & 0xFFu) << ((q & 3) * 8), __ATOMIC_RELAXED,
+        __hip_atomic_fetch_or(lds<lds_u32>((q >> 3) << 2), (c & 0xFu) << ((q & 7) * 4), __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
@@ -1238,11 +1247,12 @@ df_status check_view(const df_device_view *v, const void *dst) {
 }
 
 uint32_t out_bytes_for(df_kind kind, uint32_t max_tile_elems) {
-  if (kind == DF_KIND_U4)  // range rounded down to 32 elements, the element after it, slack, rounded to 32
-    return ((max_tile_elems + 31 + 1 + kSlack + 31) & ~31u) + 32;
+  if (kind == DF_KIND_U4)  // nibbles: range rounded down to 32 elements, the element after it,
+                           // slack, rounded to 32, one spare granule; two per byte
+    return (((max_tile_elems + 31 + 1 + kSlack<DF_KIND_U4> + 31) & ~31u) + 32) / 2;
   // tile range rounded down to a 16-element granule, plus the slack of the
   // last lane's lookahead writes, rounded to 16, plus one spare granule
-  return ((max_tile_elems + 15 + kSlack + 15) & ~15u) + 16;
+  return ((max_tile_elems + 15 + kSlack<DF_KIND_BF16> + 15) & ~15u) + 16;
 }
 
 // The first-choice counter slot of a dynamically scheduled job.  Launches

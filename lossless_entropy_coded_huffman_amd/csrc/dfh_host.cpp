@@ -296,7 +296,9 @@ void build_pair_table(const uint8_t lengths[256], const std::vector<uint16_t> &l
 
 // Multi-code decode table: entry w lists the whole codes inside the 12-bit
 // window w (first stream bit = bit 0), at most five, found by walking the
-// hierarchical tables.  Layout in include/dfh.h (section DTAB).
+// hierarchical tables.  Layout in include/dfh.h (section DTAB): symbol bytes
+// (BF16, the exponent rotated right by one bit), or for uint4 the symbols'
+// nibbles in bits 0..19, as the uint4 kernel stages them.
 void build_multi_table(df_kind kind, const std::vector<uint16_t> &lut, std::vector<uint64_t> &dtab) {
   dtab.assign(kDtabSize, 0);
   for (uint32_t w = 0; w < (uint32_t)kDtabSize; w++) {
@@ -315,6 +317,12 @@ void build_multi_table(df_kind kind, const std::vector<uint16_t> &lut, std::vect
       starts |= 1ull << pos;
       pos += l;
       count++;
+    }
+    if (kind == DF_KIND_U4) {  // nibbles of codes 0..4 | consumed bits | start flags | count
+      uint64_t nib = 0;
+      for (uint32_t i = 0; i < count; i++) nib |= ((syms >> (8 * i)) & 0xF) << (4 * i);
+      if (count) dtab[w] = nib | ((uint64_t)pos << 32) | ((starts >> 1) << 37) | ((uint64_t)count << 56);
+      continue;
     }
     // symbols 0..3 | consumed bits | start flags for bits 1..11 | symbol 4 | count
     if (count)

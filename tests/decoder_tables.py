@@ -13,7 +13,8 @@ index is the k-th stream bit): the whole codes inside the window, at most
 five, in order.  Bits 0..31 symbol bytes of codes 0..3 (BF16: the exponent
 rotated right by one bit), 32..36 bits consumed, 37..47 a flag for each code
 that starts at window bit 1..11, 48..55 symbol byte of code 4, 56..63 number
-of codes; 0 when no whole code fits.
+of codes; 0 when no whole code fits.  uint4 holds the symbols as nibbles:
+bits 0..19 the low nibbles of codes 0..4 (4 bits per code, in order).
 
 pair_table_section (uint8): u32 per 13-bit window, at most two codes: bits
 0..3 bits consumed, 8..15 and 16..23 the two symbols (0 when one), 24..31
@@ -52,6 +53,9 @@ def multicode_table(kind, lengths, codes, K=12):
             continue
         v = 0
         for i, s in enumerate(syms):
+            if kind == 2:
+                v |= (s & 0xF) << (4 * i)
+                continue
             byte = ((s >> 1) | ((s & 1) << 7)) if kind == 0 else s
             v |= byte << (8 * i if i < 4 else 48)
         flags = sum(1 << (st - 1) for st in starts if st > 0)

@@ -17,17 +17,36 @@ def window(bits):
 
 
 def test_multicode_entries_by_hand():
-    tab = multicode_table(2, LENGTHS, CODES, K=4)
+    # BF16 layout (symbol bytes, rotated right by one bit)
+    rot = {s: (s >> 1) | ((s & 1) << 7) for s in (10, 20, 30, 40)}
+    tab = multicode_table(0, LENGTHS, CODES, K=4)
     # 0000: four codes "0", starts 0..3, 4 bits
-    assert tab[window("0000")] == 10 | 10 << 8 | 10 << 16 | 10 << 24 | 4 << 32 | 0b111 << 37 | 4 << 56
+    assert tab[window("0000")] == rot[10] * 0x01010101 | 4 << 32 | 0b111 << 37 | 4 << 56
     # 1011: "10" then "11" is no whole code: one code, 2 bits
-    assert tab[window("1011")] == 20 | 2 << 32 | 1 << 56
+    assert tab[window("1011")] == rot[20] | 2 << 32 | 1 << 56
     # 0110: "0" then "110": two codes, the second starting at bit 1, 4 bits
-    assert tab[window("0110")] == 10 | 30 << 8 | 4 << 32 | 0b1 << 37 | 2 << 56
+    assert tab[window("0110")] == rot[10] | rot[30] << 8 | 4 << 32 | 0b1 << 37 | 2 << 56
     # 1110: "111" then "0": 4 bits, second code starts at bit 3
-    assert tab[window("1110")] == 40 | 10 << 8 | 4 << 32 | 0b100 << 37 | 2 << 56
+    assert tab[window("1110")] == rot[40] | rot[10] << 8 | 4 << 32 | 0b100 << 37 | 2 << 56
     # 1101 (K = 4): "110", then "1" is no whole code
-    assert tab[window("1101")] == 30 | 3 << 32 | 1 << 56
+    assert tab[window("1101")] == rot[30] | 3 << 32 | 1 << 56
+
+
+def test_multicode_uint4_nibbles_by_hand():
+    # uint4 symbols 3, 5, 9, 12 with the same lengths and codes: the symbols
+    # are nibbles, four bits per code in order
+    ln = np.zeros(256, np.uint8)
+    ln[[3, 5, 9, 12]] = [1, 2, 3, 3]
+    codes = np.zeros(256, np.uint32)
+    codes[[3, 5, 9, 12]] = [0b0, 0b10, 0b110, 0b111]
+    tab = multicode_table(2, ln, codes, K=4)
+    assert tab[window("0000")] == 0x3333 | 4 << 32 | 0b111 << 37 | 4 << 56
+    assert tab[window("1011")] == 5 | 2 << 32 | 1 << 56
+    assert tab[window("0110")] == 3 | 9 << 4 | 4 << 32 | 0b1 << 37 | 2 << 56
+    assert tab[window("1110")] == 12 | 3 << 4 | 4 << 32 | 0b100 << 37 | 2 << 56
+    assert tab[window("1101")] == 9 | 3 << 32 | 1 << 56
+    five = multicode_table(2, ln, codes, K=6)[window("000000")]
+    assert five == 0x33333 | 5 << 32 | 0b1111 << 37 | 5 << 56
 
 
 def test_multicode_fifth_code_and_bf16_rotation():
