@@ -287,6 +287,13 @@ def main():
             return [lambda: dfh.df_decompress_batch(dcs, o, stream)]
         return [lambda dc=dc: dfh.df_decompress(dc, o[0], stream) for dc in dcs]
 
+    # Python's cyclic collector runs once here and stays off through the
+    # warm-up and the timed launches: a full collection can take tens of
+    # milliseconds, several times the timed region at --steps 20, and a
+    # pause of that length just before the region lets the chip's clock
+    # drop again (measured: 7-11% slower timed launches).
+    gc.collect()
+    gc.disable()
     # Time-based warm-up first: measured per-launch times on a fresh box are
     # steady for about ten launches, 10-15% slower for the next 40 while the
     # shader clock drops under the decoder's power draw, and steady again
@@ -312,12 +319,7 @@ def main():
     # several microseconds each and would be timed as part of the decode.
     # The mean launch duration is that span over the launch count (so it
     # includes the dispatch gap between launches).
-    # Python's cyclic collector runs before the region and not inside it: a
-    # full collection can take tens of milliseconds, several times the whole
-    # region at --steps 20.
     region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    gc.collect()
-    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record(stream)
