@@ -481,6 +481,51 @@ def test_u4_batch_and_checked(torch_dev, orc):
         assert np.array_equal(host_of(o, 2), p)
 
 
+def test_u4_codes_up_to_32_bits(torch_dev, orc):
+    # an incomplete uint4 code: lengths 1..15 and one 32-bit code (Kraft sum
+    # below 1), symbols drawn uniformly, so codes past the 12-bit table (up
+    # to four table levels) are frequent and straddle chunk and tile ends,
+    # and tiles end on odd elements with long codes next
+    ln = np.zeros(256, np.uint8)
+    ln[:16] = list(range(1, 16)) + [32]
+    q = np.random.default_rng(11).integers(0, 16, 300_001).astype(np.uint8)
+    packed = synth.pack_u4(q)
+    c = dfh.df_encode(dfh.KIND_U4, packed, ln, n=q.size)
+    assert c.info()["n_luts"] >= 4
+    for checked in (True, False):
+        got, err = gpu_decode(torch_dev, c, checked)
+        assert err == 0 and np.array_equal(got, packed)
+    assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
+
+
+@pytest.mark.parametrize("cap", [1, 7, 33])
+@pytest.mark.parametrize("kind", [1, 2])
+def test_u8_u4_capped_launch(torch_dev, orc, kind, cap):
+    # a launch capped to a few workgroups runs its waves at the base priority
+    # and walks many steps per workgroup (the uint8 waves' own stores, the
+    # uint4 nibble staging)
+    torch, dev = torch_dev
+    if kind == 1:
+        want = u8_normal(2_000_003, 5)
+        c = dfh.compress(1, want)
+    else:
+        q = u4_symbols(2_000_003, 6)
+        want = synth.pack_u4(q)
+        c = dfh.compress(2, want, n=q.size)
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for checked in (False, True):
+        out.zero_()
+        if checked:
+            dfh.df_decompress_checked(dc, out, err, max_workgroups=cap)
+        else:
+            dfh.df_decompress(dc, out, max_workgroups=cap)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert np.array_equal(host_of(out, kind), want), (kind, cap, checked)
+
+
 def test_u8_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep over container sizes (1 element to 40 tiles) and symbol
     # distributions: quantised normals, uniform bytes, geometric skews whose
