@@ -417,14 +417,15 @@ __device__ __forceinline__ void store_partial(uint16_t *dst, uint32_t e0, uint32
 // ran about 5% slower.
 //
 // The pass also leaves the staging buffer zero for the next tile's ORs:
-// each lane clears the granules
-// it has just read, and the bytes from the last granule up to `dirty` (the
-// next lane-group's lookahead slack) are cleared here too.
+// each lane clears the granules it has just read, and the bytes from the
+// last granule up to `dirty` (the next lane-group's lookahead slack) are
+// cleared here too.
 //
-// uint4 packs a granule of 32 staging bytes into 16 output bytes and owns
-// the bytes whose low-nibble element is its own, [ceil(lo / 2), ceil(hi / 2))
+// uint4 staging holds nibbles in the output's packing, so a granule of 32
+// elements is 16 staging bytes copied as they are; a tile owns the output
+// bytes whose low-nibble element is its own, [ceil(lo / 2), ceil(hi / 2))
 // relative to a / 2; he is hi_r + 1 when the element after the tile exists
-// (its symbol then sits at staging position hi_r), else hi_r.
+// (its symbol then sits at staging nibble hi_r), else hi_r.
 template <int KIND>
 __device__ __forceinline__ void store_tile(const Job &jb, uint32_t buf, uint64_t a, uint32_t lo_r,
                                            uint32_t hi_r, uint32_t he, uint32_t ngroups, uint32_t dirty,
@@ -721,9 +722,10 @@ __device__ __forceinline__ v4u clean_tab(v4u v, uint32_t word, uint32_t *err) {
 template <int KIND, bool CHECKED, bool PRIO>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
-  // LDS (all dynamic, from offset 0): multi-code table, hierarchical tables,
-  // one staging buffer per tile group, the per-wave scan sums, then eight
-  // words for the dynamic schedule
+  // LDS (all dynamic, from offset 0): the decode table, hierarchical tables,
+  // one staging buffer per tile group, two sets of per-wave scan sums (32
+  // bytes per group; uint8 alternates between them), then 64 bytes for the
+  // dynamic schedule
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
