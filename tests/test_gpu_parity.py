@@ -551,6 +551,31 @@ def test_u8_random_sizes_and_distributions(torch_dev, orc):
     assert max(lengths_seen) >= 16 and min(lengths_seen) <= 2
 
 
+def test_u4_random_sizes_and_distributions(torch_dev, orc):
+    # seeded sweep over uint4 container sizes (1 element to about 40 tiles,
+    # odd and even counts) and nibble distributions: quantised normals of
+    # several widths, uniform nibbles, geometric skews (codes up to 15
+    # bits), two symbols; checked and unchecked, every case bit-exact
+    # against the packed input and the oracle's packed decode
+    rng = np.random.default_rng(4242)
+    lengths_seen = set()
+    for case in range(36):
+        n = int(rng.integers(1, 250_000)) if case % 3 else int(rng.integers(1, 3000))
+        d = case % 4
+        if d == 0:
+            q = u4_symbols(n, 900 + case, 0.5 + 3.5 * rng.random())
+        elif d == 1:
+            q = rng.integers(0, 16, n).astype(np.uint8)
+        elif d == 2:
+            q = np.minimum(rng.geometric(0.3 + 0.3 * rng.random(), n) - 1, 15).astype(np.uint8)
+        else:
+            q = rng.choice(rng.choice(16, 2, replace=False), n).astype(np.uint8)
+        say("u4 random case", case, n, d)
+        c = check_u4(torch_dev, orc, q, checked=bool(case & 1))
+        lengths_seen.add(int(c.info()["lengths"].max()))
+    assert max(lengths_seen) >= 10 and min(lengths_seen) <= 1
+
+
 def test_bf16_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep: normals of random scale, Student-t(3) tails, uniformly
     # random 16-bit patterns (every exponent), near-constant values; small
