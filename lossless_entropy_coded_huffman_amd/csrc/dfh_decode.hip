@@ -566,42 +566,42 @@ __device__ __forceinline__ uint32_t count_chunk(Stream &t, int32_t rem, uint32_t
                                                 int32_t &rem_end, uint32_t n_luts, uint32_t *err) {
   uint32_t cnt = 0, h = 0;
   if (KIND == DF_KIND_U8) {
-    // A lane past E, or at a code longer than the table's index width,
-    // takes an entry of no codes: its window stays put, so each later kept
-    // entry is empty too, and the loop below resumes the walk there.  This
+    // A lane past E takes an entry of no codes, and so does a lane at a
+    // code longer than the table's index width (staging leaves such table
+    // entries zero): its window stays put, so each later kept entry is
+    // empty too, and the loop below resumes the walk there.  This
     // branch-free form measured 3% faster on the uint8 block than the
     // guarded one below.  The bits consumed are the entry's low byte (bits
-    // 4..7 are zero: staging clears them).
+    // 4..7 are zero: staging clears them).  h is left at a zero entry only
+    // for a lane parked at a long code, whose loop below runs and sets it.
 #pragma unroll
     for (uint32_t k = 0; k < kKeep<KIND>; k++) {
+      const bool live = rem > 0;
       uint32_t y = lds<const lds_u32>(0)[t.b0 & kPairMask];
-      if (!(rem > 0 && y >= kOneCode)) y = 0;
+      if (!live) y = 0;
       drop(t, y);
       rem -= (int32_t)(y & 0xFFu);
       cnt += y >> 24;
-      if (y) h = y;
+      if (live) h = y;
       kept_lo[k] = y;
     }
   } else {
-    // the kept run ends at the lane's first code longer than the table's
-    // index width (kept as an entry of no codes); the loop below resumes
-    // the walk there.  (The branch-free form spills in the uint4 kernel at
-    // 7 kept entries and measured 2-4% slower at 5 and 6.)
-    bool parked = false;
+    // At the lane's first code longer than the table's index width the
+    // table entry is zero (staging leaves it so): the window stays put and
+    // each later kept entry is the same empty one, and the loop below
+    // resumes the walk there.  Without a separate flag for that case the
+    // uint4 block went from 71.4 to 65.2 us.  (The branch-free form spills
+    // in the uint4 kernel at 7 kept entries and measured 2-4% slower at 5
+    // and 6.)
 #pragma unroll
     for (uint32_t k = 0; k < kKeep<KIND>; k++) {
       v2u e = {0u, 0u};
-      if (rem > 0 && !parked) {
+      if (rem > 0) {
         e = lds<const lds_v2>(0)[t.b0 & (kDtabEntries - 1)];
-        if (e.y < kOneCode) {
-          e = (v2u){0u, 0u};
-          parked = true;
-        } else {
-          drop(t, e.y);
-          rem -= (int32_t)(e.y & 31);
-          cnt += e.y >> 24;
-          h = e.y;
-        }
+        drop(t, e.y);
+        rem -= (int32_t)(e.y & 31);
+        cnt += e.y >> 24;
+        h = e.y;
       }
       kept_lo[k] = e.x;
       if (k & 1) kept_hi[k / 2] |= e.y & 0xFFFF0000u;
@@ -680,7 +680,9 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
 // codes but consumes no bits would never move a walk forward, so it is
 // cleared (a cleared entry sends the walk to the hierarchical tables, which
 // consume at least one bit per code) and, in checked launches, reported as
-// DF_DEVERR_CODE.  Tables built by the library never hold such entries; a
+// DF_DEVERR_CODE.  An entry that claims no codes (a window whose first code
+// is longer than the index width) is cleared whole, so the kept runs of
+// phase 1 can take it as is: it moves nothing and counts nothing.  Tables built by the library never hold such entries; a
 // caller-made view with a damaged table pointer may.  Entries: BF16 and
 // uint4 two u64 (high words y and w), uint8 four u32 pair entries (the
 // lengths that follow the pair table are left alone), whose bits 5..7 are
@@ -697,6 +699,7 @@ __device__ __forceinline__ v4u clean_tab(v4u v, uint32_t word, uint32_t *err) {
           v[c] = 0;
           bad = true;
         }
+        if (v[c] < kOneCode) v[c] = 0;
         v[c] &= ~0xE0u;
       }
     }
@@ -709,6 +712,8 @@ __device__ __forceinline__ v4u clean_tab(v4u v, uint32_t word, uint32_t *err) {
       v.z = v.w = 0;
       bad = true;
     }
+    if (v.y < kOneCode) v.x = v.y = 0;
+    if (v.w < kOneCode) v.z = v.w = 0;
   }
   if (CHECKED && bad) atomicOr(err, DF_DEVERR_CODE);
   return v;
