@@ -29,13 +29,15 @@
 //     gap field): at 6.6-bit codes a chunk holds ten codes, and the step's
 //     fixed cost (loads, offsets, scan, barriers) is then spread over
 //     twenty;
-//   - a BF16 or uint4 group stores a tile one step late: the store pass of
-//     tile k shares a barrier interval with the count of tile k + 1, so HBM
-//     traffic overlaps the decode; the sign|mantissa bytes it merges are
-//     requested at the top of the step, before the count.  A uint8 wave
-//     stores its own lanes' output range as soon as its phase 2 is done
-//     (plain byte staging needs no clearing, so no group barrier ends the
-//     step);
+//   - a BF16 or uint4 group stores a tile one step late.  BF16: the store
+//     pass of tile k shares a barrier interval with the count of tile k + 1,
+//     so HBM traffic overlaps the decode; the sign|mantissa bytes it merges
+//     are requested at the top of the step, before the count.  uint4: the
+//     store pass of tile k runs after the scan barrier of tile k + 1, from
+//     the other of the group's two staging buffers, so no group barrier
+//     ends the step.  A uint8 wave stores its own lanes' output range as
+//     soon as its phase 2 is done (plain byte staging needs no clearing, so
+//     no group barrier ends the step either);
 //   - a lane holds its 8 stream bytes plus the next 4 (uint4: its 16 bytes;
 //     uint8: its 16 bytes plus the next 4) in registers and walks each chunk
 //     as a 96-bit window shifted with funnel shifts;
@@ -88,6 +90,10 @@ constexpr int kWaitVm0 = 0x0F70;
 // of one OR; uint4 nibbles, the two words of one OR (16 nibbles)
 template <int KIND>
 constexpr uint32_t kSlack = KIND == DF_KIND_U4 ? 16u : 12u;
+// Staging buffers per tile group: uint4 two, used by step parity (its steps
+// end without a barrier), BF16 and uint8 one.
+template <int KIND>
+constexpr uint32_t kBufs = KIND == DF_KIND_U4 ? 2u : 1u;
 // Table entries phase 1 keeps in registers for phase 2 to replay; a lane
 // with more walks the rest of its chunk again from where the kept ones end.
 // Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
@@ -728,9 +734,9 @@ template <int KIND, bool CHECKED, bool PRIO>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_kernel(const Batch batch) {
   // LDS (all dynamic, from offset 0): the decode table, hierarchical tables,
-  // one staging buffer per tile group, two sets of per-wave scan sums (32
-  // bytes per group; uint8 alternates between them), then 64 bytes for the
-  // dynamic schedule
+  // the staging buffers of each tile group (uint4 two), two sets of
+  // per-wave scan sums (32 bytes per group; uint8 and uint4 alternate between
+  // them), then 64 bytes for the dynamic schedule
   const uint32_t wg = blockIdx.x;
   uint32_t j = 0;
   while (j + 1 < batch.count && wg >= batch.job[j + 1].wg_begin) j++;
@@ -741,8 +747,8 @@ void decode_kernel(const Batch batch) {
   const uint32_t lane = tid % kTPB;
   const uint32_t n_luts = jb.n_luts;
   const uint32_t out_bytes = batch.out_bytes;
-  const uint32_t buf = kTabBytes<KIND> + batch.lut_bytes + grp * out_bytes;  // LDS byte offset
-  lds_u32 *wsum = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes);
+  const uint32_t buf0 = kTabBytes<KIND> + batch.lut_bytes + grp * kBufs<KIND> * out_bytes;  // LDS byte offset
+  lds_u32 *wsum = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * kBufs<KIND> * out_bytes);
 
   // dynamic schedule (BF16): the job's first workgroup claims a counter
   // slot, the others look for its key (requested behind the table loads
@@ -812,7 +818,7 @@ void decode_kernel(const Batch batch) {
   // unit stride, 6 the counter's last value, 7 the counter c, plus 16 once
   // its last value has been taken, plus 32 when the workgroup deals units to
   // itself, 8..9 the key, 10 the number of counters
-  lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * out_bytes + 32 * groups);
+  lds_u32 *nx_lds = lds<lds_u32>(kTabBytes<KIND> + batch.lut_bytes + groups * kBufs<KIND> * out_bytes + 32 * groups);
   if (dyn && tid == 0) {
     const uint32_t nwg = jb.wg_count, w = wg - jb.wg_begin;
     const uint32_t parts = nwg / 8 < kParts ? (nwg / 8 ? nwg / 8 : 1u) : kParts;
@@ -856,16 +862,20 @@ void decode_kernel(const Batch batch) {
     nhi = tout[C * (base + grp) + C < n_tiles ? C * (base + grp) + C : n_tiles];
   }
   {  // the staging buffer starts zero (out_bytes is a multiple of 16)
-    lds_v4 *z = lds<lds_v4>(buf);
-    for (uint32_t i = lane; i < out_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
+    lds_v4 *z = lds<lds_v4>(buf0);
+    for (uint32_t i = lane; i < kBufs<KIND> * out_bytes / 16; i += kTPB) z[i] = (v4u){0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
-  // The previous tile of this group is stored one step late, while this
-  // step counts: the store pass (HBM-heavy) then shares a barrier interval
-  // with phase 1 (LDS- and ALU-heavy).  It reads the staging buffer before
-  // phase 2 writes it again (a barrier lies between) and clears what it
-  // reads, so one buffer per group suffices.
+  // The previous tile of this group is stored one step late.  BF16: while
+  // this step counts, so the store pass (HBM-heavy) shares a barrier
+  // interval with phase 1 (LDS- and ALU-heavy); it reads the staging buffer
+  // before phase 2 writes it again (a barrier lies between) and clears what
+  // it reads, so one buffer per group suffices.  uint4: right after the scan
+  // barrier, from the other of its two buffers, which phase 2 writes again
+  // only after the next scan barrier; so the step needs no barrier at its
+  // end (uint4 block 65.0 -> 61.3 us side by side; the store after phase 2
+  // instead, 63.7 us).
   bool have_prev = false;
   uint64_t prev_a = 0;
   uint32_t prev_lo = 0, prev_hi = 0, prev_he = 0, prev_ng = 0, prev_dirty = 0;
@@ -873,6 +883,8 @@ void decode_kernel(const Batch batch) {
   uint32_t par = 0;  // step parity
   for (; base < n_spans;) {
     const uint32_t tile = base + grp;  // the span, wave-uniform
+    const uint32_t buf = buf0 + (kBufs<KIND> == 2 ? par * out_bytes : 0u);  // this step's staging
+    const uint32_t pbuf = buf0 + (kBufs<KIND> == 2 ? (par ^ 1u) * out_bytes : 0u);  // the previous step's
     const bool active = tile < n_spans;
     // The previous tile's first sign|mantissa granules go in flight first
     // (granules past the tile read its last one; step 0 reads granule 0),
@@ -963,24 +975,24 @@ void decode_kernel(const Batch batch) {
     // in flight, and the store pass starts with no other load outstanding.
 #pragma unroll
     for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-    if constexpr (KIND != DF_KIND_U8) {
+    if constexpr (KIND == DF_KIND_BF16) {
       if (have_prev)
         store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
+      have_prev = active;
+      prev_a = a;
+      prev_lo = lo_r;
+      prev_hi = hi_r;
+      prev_he = hi_r + (hi < jb.n ? 1u : 0u);
+      prev_ng = ngroups;
     }
-    have_prev = KIND != DF_KIND_U8 && active;
-    prev_a = a;
-    prev_lo = lo_r;
-    prev_hi = hi_r;
-    prev_he = hi_r + (hi < jb.n ? 1u : 0u);
-    prev_ng = ngroups;
 
     // prefix sum of the counts over the tile's 256 lanes
     const uint32_t wid = tid >> 6;
     const uint32_t x = wave_inclusive_sum(cnt);
-    // (uint8: two sets of sums, by step parity: its steps end without a
-    // barrier, so a wave may write next step's sums while another still
-    // reads these)
-    const uint32_t wset = KIND == DF_KIND_U8 ? 4 * groups * par : 0u;
+    // (uint8 and uint4: two sets of sums, by step parity: their steps end
+    // without a barrier, so a wave may write next step's sums while another
+    // still reads these)
+    const uint32_t wset = KIND != DF_KIND_BF16 ? 4 * groups * par : 0u;
     if ((tid & 63) == 63) wsum[wset + wid] = x;
     if (dyn && tid == 0) {  // last step's grab, for the workgroup: its first tile
       uint32_t pub = 0xFFFFFFFFu;  // no tile: past any span index
@@ -1029,6 +1041,16 @@ void decode_kernel(const Batch batch) {
     const uint32_t off = (wq > 0 ? s0 : 0u) + (wq > 1 ? s1 : 0u) + (wq > 2 ? s2 : 0u) + x - cnt;
     if (CHECKED && active && lane == 0 && s0 + s1 + s2 + s3 != hi_r - lo_r)
       atomicOr(batch.err, DF_DEVERR_COUNT);
+    if constexpr (KIND == DF_KIND_U4) {  // the previous tile (its phase 2 ended before the scan barrier)
+      if (have_prev)
+        store_tile<KIND>(jb, pbuf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
+      have_prev = active;
+      prev_a = a;
+      prev_lo = lo_r;
+      prev_hi = hi_r;
+      prev_he = hi_r + (hi < jb.n ? 1u : 0u);
+      prev_ng = ngroups;
+    }
     {  // staging bytes phase 2 may write: every lane ends by lo_r + off + cnt
        // + the slack (uint4: nibbles, two per byte)
       const uint32_t e = lo_r + s0 + s1 + s2 + s3 + kSlack<KIND>;
@@ -1121,7 +1143,7 @@ void decode_kernel(const Batch batch) {
           if (p >= r0 && p < r1 && (p < 16 * fs || p >= 16 * fe)) dst_t[p] = *lds<const lds_u8>(buf + p);
         }
       }
-    } else {
+    } else if constexpr (kBufs<KIND> == 1) {
       __syncthreads();
     }
     par ^= 1u;
@@ -1137,6 +1159,7 @@ void decode_kernel(const Batch batch) {
   if (dyn && tid == 0 && (nx_lds[7] & 16) && nx_lds[1] != kNoTicket) counter_finished(nx_lds[1], nx_lds[10]);
   // the last tile of this group (BF16 and uint4)
   if constexpr (KIND != DF_KIND_U8) {
+    if (kBufs<KIND> == 2) __syncthreads();  // (the loop's exit is uniform over the workgroup)
     if (have_prev) {
       uint2 smv[kPrefetch];
 #pragma unroll
@@ -1147,7 +1170,8 @@ void decode_kernel(const Batch batch) {
       }
 #pragma unroll
       for (uint32_t k = 0; k < kPrefetch; k++) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
-      store_tile<KIND>(jb, buf, prev_a, prev_lo, prev_hi, prev_he, prev_ng, prev_dirty, smv, lane);
+      store_tile<KIND>(jb, buf0 + (kBufs<KIND> == 2 ? (par ^ 1u) * out_bytes : 0u), prev_a, prev_lo, prev_hi,
+                       prev_he, prev_ng, prev_dirty, smv, lane);
     }
   }
 }
@@ -1315,7 +1339,7 @@ df_status launch(const df_device_view *views, void *const *dsts, uint32_t count,
     size_t lds = 0;
     for (uint32_t g = kMaxGroups; g >= 1; g--) {
       const size_t need = (size_t)(kind == DF_KIND_U8 ? kTabBytes<DF_KIND_U8> : kDtabBytes) + lut_bytes +
-                          (size_t)g * out_bytes + 32 * g + 64;
+                          (size_t)g * out_bytes * (kind == DF_KIND_U4 ? kBufs<DF_KIND_U4> : 1u) + 32 * g + 64;
       if (need > (size_t)props.max_lds) continue;
       int occ = 0;
       if (occupancy(props.dev, fn, (int)(g * kTPB), need, &occ) != DF_OK) return DF_ERR_HIP;
