@@ -641,3 +641,45 @@ def test_table_entries_that_consume_no_bits(torch_dev, orc, kind):
         say("damaged table", kind, "checked", checked, "err", int(err.item()))
         assert np.array_equal(host_of(out, kind), src)
         assert int(err.item()) == (dfh.DEVERR_CODE if checked else 0)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_table_entries_that_hold_no_codes(torch_dev, orc, kind):
+    """Every entry of the decoder-side table replaced from the host by one
+    that claims no codes but carries other bits (a consumed-bit field, symbol
+    bytes, start flags).  The library's tables hold zero there; the kernel
+    clears such entries whole while staging the table, and its kept runs take
+    a cleared entry as one that moves nothing, so every code takes the
+    hierarchical tables (intact here): the output is still the input, with no
+    error reported."""
+    torch, dev = torch_dev
+    n = 2_000_003
+    if kind == 0:
+        src = bf16_normal(n, 44)
+        c = dfh.compress(0, src)
+    elif kind == 1:
+        src = u8_normal(n, 45, False)
+        c = dfh.compress(1, src)
+    else:
+        q = u4_symbols(n, 46)
+        src = synth.pack_u4(q)
+        c = dfh.compress(2, src, n=n)
+    dc = dfh.to_device(c, dev)
+    tab = dc.sections["dtab"]
+    if kind == 1:   # uint8: 8192 u32 pair entries, count 0, every other bit set
+        tab[: 4 * 8192].view(torch.int32).fill_(0x00FFFFFF)
+    else:           # u64 entries: high word count 0, other bits set; low word set
+        w = tab[: 8 * 4096].view(torch.int32).view(-1, 2)
+        w[:, 0].fill_(-1)
+        w[:, 1].fill_(0x00FFFFFF)
+    for checked in (False, True):
+        out = dc.empty_output()
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        if checked:
+            dfh.df_decompress_checked(dc, out, err)
+        else:
+            dfh.df_decompress(dc, out)
+        torch.cuda.synchronize()
+        say("no-code table entries", kind, "checked", checked, "err", int(err.item()))
+        assert np.array_equal(host_of(out, kind), src)
+        assert int(err.item()) == 0
