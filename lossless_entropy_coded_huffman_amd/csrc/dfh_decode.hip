@@ -925,12 +925,23 @@ void decode_kernel(const Batch batch) {
     // chunk bounds: codes start in [gap, E) of this lane's (first) 64
     // stream bits, and in [gap2, E2) of its second chunk (uint8)
     uint32_t gap = 0, E = 0, gap2 = 0, E2 = 0;
-    if (active) {
+    const uint64_t bits_left = jb.total_bits - (uint64_t)tile * (64 * C * kTPB);  // uniform
+    if (KIND != DF_KIND_BF16 && active && __builtin_expect(bits_left >= 64 * (uint64_t)(C * kTPB), 1)) {
+      // a whole span (all but a container's last): every lane has all its
+      // chunks, 64 bits each, so no lane needs the per-lane bounds below
+      // (uint8 and uint4 -1.3% and -1.6%; BF16 measured 0.4% slower with it)
+      const uint32_t f = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * C * lane) & 31));
+      gap = f & 31u;
+      E = 64;
+      if (C == 2) {
+        gap2 = (f >> 5) & 31u;
+        E2 = 64;
+      }
+    } else if (active) {
       const uint64_t chunks_left = jb.n_threads - (uint64_t)tile * (C * kTPB);  // > 0 for an active span
       if (C * lane < chunks_left) {
         const uint32_t f = (uint32_t)(((((uint64_t)cur.g1) << 32) | cur.g0) >> ((5 * C * lane) & 31));
         gap = f & 31u;
-        const uint64_t bits_left = jb.total_bits - (uint64_t)tile * (64 * C * kTPB);
         if (bits_left >= 64 * (uint64_t)(C * kTPB)) {
           E = 64;
           E2 = C == 2 ? 64u : 0u;
