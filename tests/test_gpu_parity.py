@@ -526,6 +526,36 @@ def test_u8_u4_capped_launch(torch_dev, orc, kind, cap):
         assert np.array_equal(host_of(out, kind), want), (kind, cap, checked)
 
 
+@pytest.mark.parametrize("cap", [0, 1, 5])
+def test_u4_large_tiles_many_steps(torch_dev, orc, cap):
+    # one symbol in 99.5% of the elements: 1-bit codes, tiles of close to
+    # 16384 elements, so each group's two staging buffers are near their
+    # largest (the launch then fits fewer groups or workgroups per CU), and
+    # capped launches walk many steps per group, the buffers alternating
+    torch, dev = torch_dev
+    rng = np.random.default_rng(70 + cap)
+    q = np.full(3_000_001, 5, np.uint8)
+    pick = rng.random(q.size) < 0.005
+    q[pick] = rng.integers(0, 16, int(pick.sum()))
+    want = synth.pack_u4(q)
+    c = dfh.compress(2, want, n=q.size)
+    assert int(c.info()["max_tile_elems"]) > 14000
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for checked in (False, True):
+        out.zero_()
+        if checked:
+            dfh.df_decompress_checked(dc, out, err, max_workgroups=cap)
+        else:
+            dfh.df_decompress(dc, out, max_workgroups=cap)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        got = host_of(out, 2)
+        assert np.array_equal(got, want), (cap, checked)
+    assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
+
+
 def test_u8_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep over container sizes (1 element to 40 tiles) and symbol
     # distributions: quantised normals, uniform bytes, geometric skews whose
