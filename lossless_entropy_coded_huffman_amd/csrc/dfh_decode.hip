@@ -97,9 +97,10 @@ constexpr uint32_t kBufs = KIND == DF_KIND_U4 ? 2u : 1u;
 // Table entries phase 1 keeps in registers for phase 2 to replay; a lane
 // with more walks the rest of its chunk again from where the kept ones end.
 // Counts measured per kind: uint4 keeps 7 (a lane walks about 6 entries at
-// 2.7-bit codes), uint8 5 of its pair-table words per chunk (every unrolled
-// step costs the whole wave, and the uint8 kernel is bound by VALU issue;
-// 5 measured 0.5% faster than 4 and 1.5% faster than 6),
+// 2.7-bit codes; 6 and 8 measured 1.6% and 0.8% slower), uint8 5 of its
+// pair-table words per chunk (every unrolled step costs the whole wave, and
+// the uint8 kernel is bound by VALU issue; 4 and 6 measured 1.0% and 0.7%
+// slower),
 // BF16 none (its sign|mantissa prefetch holds the registers: with one or two
 // kept entries the kernel spills to scratch).
 template <int KIND>
@@ -596,9 +597,9 @@ __device__ __forceinline__ uint32_t count_chunk(Stream &t, int32_t rem, uint32_t
     // table entry is zero (staging leaves it so): the window stays put and
     // each later kept entry is the same empty one, and the loop below
     // resumes the walk there.  Without a separate flag for that case the
-    // uint4 block went from 71.4 to 65.2 us.  (The branch-free form spills
-    // in the uint4 kernel at 7 kept entries and measured 2-4% slower at 5
-    // and 6.)
+    // uint4 block went from 71.4 to 65.2 us.  (The branch-free form, every
+    // kept lookup in every lane, measured 68.3 against 65.1 us: a lane past
+    // the chunk end skips its remaining lookups here, and their LDS reads.)
 #pragma unroll
     for (uint32_t k = 0; k < kKeep<KIND>; k++) {
       v2u e = {0u, 0u};
