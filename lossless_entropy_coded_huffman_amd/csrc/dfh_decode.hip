@@ -687,10 +687,11 @@ __device__ __forceinline__ uint32_t write_chunk(uint32_t q, uint32_t qend, Strea
 // codes but consumes no bits would never move a walk forward, so it is
 // cleared (a cleared entry sends the walk to the hierarchical tables, which
 // consume at least one bit per code) and, in checked launches, reported as
-// DF_DEVERR_CODE.  An entry that claims no codes (a window whose first code
-// is longer than the index width) is cleared whole, so the kept runs of
-// phase 1 can take it as is: it moves nothing and counts nothing.  Tables built by the library never hold such entries; a
-// caller-made view with a damaged table pointer may.  Entries: BF16 and
+// DF_DEVERR_CODE.  Tables built by the library never hold such entries; a
+// caller-made view with a damaged table pointer may.  An entry that claims
+// no codes (a window whose first code is longer than the index width) is
+// cleared whole (the library's are zero already), so the kept runs of
+// phase 1 can take it as is: it moves nothing and counts nothing.  Entries: BF16 and
 // uint4 two u64 (high words y and w), uint8 four u32 pair entries (the
 // lengths that follow the pair table are left alone), whose bits 5..7 are
 // cleared as well: phase 1 reads an entry's bits consumed as its low byte,
