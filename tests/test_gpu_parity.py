@@ -556,6 +556,28 @@ def test_u4_large_tiles_many_steps(torch_dev, orc, cap):
     assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
 
 
+def test_u4_batch_of_large_and_small_tiles(torch_dev, orc):
+    # one launch over containers whose tiles differ four-fold in size: the
+    # staging buffers (two per group) are sized by the largest, and each
+    # container's tiles are checked against its own input and the oracle
+    torch, dev = torch_dev
+    rng = np.random.default_rng(81)
+    qs = [np.full(1_000_003, 9, np.uint8), rng.integers(0, 16, 700_001).astype(np.uint8),
+          np.clip(np.rint(rng.normal(7.5, 2.2, 900_002)), 0, 15).astype(np.uint8)]
+    qs[0][rng.random(qs[0].size) < 0.004] = 3
+    cs = [dfh.compress(dfh.KIND_U4, synth.pack_u4(q), n=q.size) for q in qs]
+    sizes = [int(c.info()["max_tile_elems"]) for c in cs]
+    assert max(sizes) > 3 * min(sizes)
+    dcs = [dfh.to_device(c, dev) for c in cs]
+    outs = [dc.empty_output() for dc in dcs]
+    dfh.df_decompress_batch(dcs, outs)
+    torch.cuda.synchronize()
+    for q, c, o in zip(qs, cs, outs):
+        got = host_of(o, 2)
+        assert np.array_equal(got, synth.pack_u4(q))
+        assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
+
+
 def test_u8_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep over container sizes (1 element to 40 tiles) and symbol
     # distributions: quantised normals, uniform bytes, geometric skews whose
