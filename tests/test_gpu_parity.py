@@ -578,6 +578,35 @@ def test_u4_batch_of_large_and_small_tiles(torch_dev, orc):
         assert np.array_equal(got, orc.pack_u4(orc.decode_tiles(oracle_container(c), 8)))
 
 
+@pytest.mark.parametrize("cap", [0, 1, 5])
+def test_u8_large_tiles_many_steps(torch_dev, orc, cap):
+    # one byte value in 99.5% of the elements: 1-bit codes, tile pairs of
+    # close to 32768 elements, so a group's staging is near its largest and
+    # the launch fits fewer groups per CU; capped launches walk many steps
+    # per wave (each wave's own store of its range)
+    torch, dev = torch_dev
+    rng = np.random.default_rng(90 + cap)
+    want = np.full(3_000_001, 131, np.uint8)
+    pick = rng.random(want.size) < 0.005
+    want[pick] = rng.integers(120, 128, int(pick.sum()))  # (255 rare values would need over 64 table levels)
+    c = dfh.compress(1, want)
+    assert int(c.info()["max_tile_elems"]) > 14000
+    dc = dfh.to_device(c, dev)
+    out = dc.empty_output()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for checked in (False, True):
+        out.zero_()
+        if checked:
+            dfh.df_decompress_checked(dc, out, err, max_workgroups=cap)
+        else:
+            dfh.df_decompress(dc, out, max_workgroups=cap)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        got = host_of(out, 1)
+        assert np.array_equal(got, want), (cap, checked)
+    assert np.array_equal(got, orc.decode_tiles(oracle_container(c), 8))
+
+
 def test_u8_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep over container sizes (1 element to 40 tiles) and symbol
     # distributions: quantised normals, uniform bytes, geometric skews whose
