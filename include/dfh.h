@@ -159,13 +159,16 @@ df_status df_histogram(df_kind kind, const void *src, uint64_t n, uint64_t hist[
  * optimal max_len-limited lengths by package-merge.  One used symbol gets
  * length 1; none gives all zeros.  lengths[s] = 0 for unused symbols.
  * DF_ERR_ARG for max_len outside 1..32; DF_ERR_CODEBOOK when 2^max_len is
- * below the number of used symbols. */
+ * below the number of used symbols, or when the codes would need more than
+ * DF_MAX_LUTS hierarchical tables (a histogram with one dominant symbol and
+ * very many rare ones, whose long codes spread over many 8-bit prefixes). */
 df_status df_build_codebook(const uint64_t hist[256], uint32_t max_len, uint8_t lengths[256]);
 
 /* Encode n elements with the given lengths into a new container (*out,
  * freed with df_container_free).  Builds every section described above.
- * DF_ERR_CODEBOOK when an element's symbol has length 0 or lengths violate
- * Kraft's inequality or exceed 32; DF_ERR_ALLOC on allocation failure. */
+ * DF_ERR_CODEBOOK when an element's symbol has length 0, lengths violate
+ * Kraft's inequality or exceed 32, or the codes need more than DF_MAX_LUTS
+ * hierarchical tables; DF_ERR_ALLOC on allocation failure. */
 df_status df_encode(df_kind kind, const void *src, uint64_t n, const uint8_t lengths[256],
                     df_container **out);
 

@@ -296,3 +296,22 @@ def test_decompress_argument_checks_run_before_any_device_call():
     t = 3
     assert call(t, 1, 64) == -1                       # n_threads below (n_tiles - 1) * 256
     assert call(t, 2 * 256 + 1, 40) == -1             # total_bits below the last thread's start
+
+
+def test_codebook_beyond_the_table_cap_is_refused():
+    # one dominant byte value and every other value rare: the rare values'
+    # long codes spread over more 8-bit prefixes than DF_MAX_LUTS tables
+    # hold, so the codebook is refused (DF_ERR_CODEBOOK) rather than built
+    # into a container the decoder cannot stage; with eight rare values the
+    # same skew needs one table
+    rng = np.random.default_rng(12)
+    x = np.full(3_000_001, 131, np.uint8)
+    pick = rng.random(x.size) < 0.005
+    x[pick] = rng.integers(0, 256, int(pick.sum()))
+    h = dfh.df_histogram(dfh.KIND_U8, x)
+    with pytest.raises(dfh.DFError) as e:
+        dfh.df_build_codebook(h)
+    assert e.value.status == -3
+    x[pick] = rng.integers(120, 128, int(pick.sum()))
+    c = dfh.compress(dfh.KIND_U8, x)
+    assert c.info()["n_luts"] == 1
