@@ -632,6 +632,40 @@ def test_u8_random_sizes_and_distributions(torch_dev, orc):
     assert max(lengths_seen) >= 16 and min(lengths_seen) <= 2
 
 
+@pytest.mark.parametrize("checked", [True, False])
+def test_u4_corrupt_tile_is_contained(torch_dev, checked):
+    # as for BF16 and uint8, with uint4's two staging buffers per group: one
+    # lane's 64 stream bits in one tile set to ones (the longest code over
+    # and over), so the tile's code count no longer matches its offsets.
+    # Every output byte outside the corrupt tile and the tile before it
+    # (whose last lane reads ahead into it, and which may share its last byte
+    # with it) is exact: the corrupt tile leaves nothing behind in either
+    # buffer for the tiles after it
+    torch, dev = torch_dev
+    q = u4_symbols(30_000_001, 14)
+    want = synth.pack_u4(q)
+    c = dfh.compress(2, want, n=q.size)
+    nt = int(c.info()["n_tiles"])
+    assert nt > 4096
+    to = np.asarray(c.section("tile_out")).astype(np.int64)
+    dc = dfh.to_device(c, dev)
+    t = nt // 3
+    bits = dc.sections["bitstream"].view(torch.int32)
+    bits[t * 512 + 300: t * 512 + 302] = -1
+    out = dc.empty_output()
+    if checked:
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        dfh.df_decompress_checked(dc, out, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) != 0
+    else:
+        dfh.df_decompress(dc, out)
+    got = host_of(out, 2)
+    lo, hi = int(to[t - 1]) // 2, (int(to[t + 1]) + 1) // 2
+    assert np.array_equal(got[:lo], want[:lo])
+    assert np.array_equal(got[hi:], want[hi:])
+
+
 def test_u4_random_sizes_and_distributions(torch_dev, orc):
     # seeded sweep over uint4 container sizes (1 element to about 40 tiles,
     # odd and even counts) and nibble distributions: quantised normals of
