@@ -179,8 +179,8 @@ def cpu_baseline(containers, srcs, kind):
         "value_1thread": round(out_bytes_of(kind, d0["n"]) / t_1 / 1e9, 4), "verified": bool(ok),
         "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
         "host_cpus_usable": len(os.sched_getaffinity(0)),
-        "cores_note": "threads = the CPUs this process may use, at most 16 (one GPU's share of "
-                      "the host on the GPU boxes this runs on)",
+        "cores_note": "threads = the CPUs this process may use, at most 16 (the host CPU share "
+                      "that comes with one GPU on the one-GPU hosts this runs on)",
     }
 
 
